@@ -1,0 +1,203 @@
+"""Parallel-draft step benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one whole parallel-draft round on a seeded synthetic batch whose
+inputs already sit in HBM: batch expansion + hidden placement
+(prepare_draft_batch), the single drafter pass with LM head and argmax
+(draft_forward) and greedy acceptance (accept).  The value is draft tokens
+per second (c * K tokens per step).  One JSON line is printed, with the
+roofline of the dominant kernel (the LM head) measured with HIP events on its
+own stream during the timed steps, and the CPU oracle timed on the host on a
+bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "draft tokens/s per parallel-draft step (K=7, c=1/64); % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lm_head_traffic.json")
+
+
+def _src_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("gemv.hip", "common.h"):
+        with open(os.path.join(ROOT, "drafting_draft_expand_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def lm_head_bytes(spec, S: int) -> int:
+    """Algorithmic HBM bytes of one LM-head launch: every vocabulary row of the
+    weight once (H elements each) plus the S normalised activation rows."""
+    eb = 4 if spec.dtype == "fp32" else 2
+    return spec.vocab * spec.hidden * eb + S * spec.hidden * eb
+
+
+def step_bytes(spec, wl, b) -> int:
+    """Algorithmic bytes of one whole round (weights once, KV read once per
+    (sequence, kv head), hidden/metadata once)."""
+    eb = 4 if spec.dtype == "fp32" else 2
+    H, d = spec.hidden, spec.head_dim
+    qd, kvd = spec.n_q * d, spec.n_kv * d
+    w = 2 * H * H + spec.n_layers * (H * (qd + 2 * kvd) + qd * H + 3 * H * spec.inter) + spec.vocab * H
+    kv_read = 0
+    for i in range(b.c):
+        kv_len = int(b.target_pos[int(b.query_lens[:i].sum()) + int(b.num_accepted[i])]) + b.K
+        kv_read += kv_len * kvd * 2 * spec.n_layers
+    T, N = b.T, b.N
+    hid = (T * H + N * H) * eb          # placement read + write
+    emb = N * H * eb                     # embedding rows gathered
+    return (w + kv_read) * eb + hid + emb
+
+
+def _cpu_baseline(wl, w, b, budget_s: float):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    u, alt = __import__("synth").make_agreement_draws(wl)
+    rounds = 0
+    t0 = time.perf_counter()
+    while True:
+        r = oracle.parallel_draft_step(wl.model, w, b, want_logits=False)
+        tgt = __import__("synth").target_tokens_from_drafts(r["forward"]["tokens"], u, alt, wl.agree_probs(),
+                                                              wl.model.vocab)
+        oracle.accept(r["forward"]["tokens"], tgt)
+        rounds += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or rounds >= 20:
+            break
+    del np
+    return dict(value=round(rounds * wl.c * wl.K / el, 3), unit="draft tokens/s", cores=int(threads),
+                kind="oracle",
+                sample=f"{rounds} full round(s) of {wl.name} through the float64 oracle "
+                       f"(expand, placement, drafter pass, argmax, acceptance), {el:.1f} s")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gptoss20b-bf16-c1-k7")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        return 2
+
+    import torch
+    import drafting_draft_expand_amd as pe
+    import synth
+    from synth.device import to_torch, upload_batch, upload_weights
+
+    wl = synth.WORKLOADS[args.workload]
+    spec = wl.model
+    dev = "cuda:0"
+    t_setup = time.perf_counter()
+    w = synth.make_weights(spec, wl.wseed)
+    b = synth.make_batch(wl)
+    dw = upload_weights(w, dev)
+    db = upload_batch(b, dev)
+    model = pe.DraftModel.from_spec(spec, dw)
+    rng = __import__("numpy").random.default_rng(wl.seed + 99)
+    tgt = to_torch(rng.integers(0, spec.vocab - 1, size=(wl.c, wl.K + 1)), device=dev)
+    c, K, T, N = wl.c, wl.K, b.T, b.N
+    prep = pe.prepare_draft_batch(model, K, db["query_lens"], db["target_ids"], db["target_pos"],
+                                  db["num_accepted"], db["bonus_ids"], db["target_hidden"], db["block_table"])
+    ws = torch.empty(model.workspace_bytes(c, K, N), dtype=torch.uint8, device=dev)
+    tokens = torch.empty((c, K), dtype=torch.int32, device=dev)
+    acc = torch.empty(c, dtype=torch.int32, device=dev)
+    bonus = torch.empty(c, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    print(f"# setup {time.perf_counter() - t_setup:.1f}s workload={wl.name} N={N} T={T}", file=sys.stderr,
+          flush=True)
+
+    def step():
+        pe.prepare_draft_batch(model, K, db["query_lens"], db["target_ids"], db["target_pos"], db["num_accepted"],
+                               db["bonus_ids"], db["target_hidden"], db["block_table"], out=prep, stream=stream)
+        pe.draft_forward(model, prep, db["block_table"], db["k_cache"], db["v_cache"], workspace=ws,
+                         tokens=tokens, stream=stream)
+        pe.accept(tokens, tgt, acc, bonus, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    model.timing_enable(pe.PE_KERNEL_LM_HEAD, True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    lm_ms, lm_n = model.timing_read(pe.PE_KERNEL_LM_HEAD)
+    model.timing_enable(pe.PE_KERNEL_LM_HEAD, False)
+    ms_per_step = total_ms / args.steps
+    value = c * K / (ms_per_step / 1e3)
+    print(f"# timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step; lm-head {lm_ms / max(lm_n, 1) * 1e3:.1f} us "
+          f"x {lm_n}", file=sys.stderr, flush=True)
+
+    lm_avg_s = lm_ms / max(lm_n, 1) / 1e3
+    lm_b = lm_head_bytes(spec, c * K)
+    achieved = lm_b / lm_avg_s / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tf = json.load(open(TRAFFIC_FILE))
+        rec = tf.get(wl.name)
+        if rec and rec.get("src_hash") == _src_hash():
+            traffic = rec.get("bytes_per_launch")
+    sb = step_bytes(spec, wl, b)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "draft tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if spec.dtype == "bf16" else "f32",
+        "data": "synthetic: seeded N(0,0.02) weights, N(0,1) target hidden states and cached KV, "
+                "uniform accepted counts",
+        "config": {"workload": wl.name, "num_seqs": c, "draft_depth": K, "draft_rows": N, "sampled_rows": c * K,
+                   "hidden": spec.hidden, "vocab": spec.vocab, "layers": spec.n_layers,
+                   "q_heads": spec.n_q, "kv_heads": spec.n_kv, "head_dim": spec.head_dim,
+                   "intermediate": spec.inter, "context": [int(b.context.min()), int(b.context.max())]},
+        "roofline": {"bound": "hbm", "kernel": "lm_head_argmax", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": lm_b,
+                     "avg_launch_us": round(lm_avg_s * 1e6, 2), "launches": lm_n},
+        "step_roofline": {"bound": "hbm", "algorithmic_bytes": sb,
+                          "achieved": round(sb / (ms_per_step / 1e3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(sb / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = _cpu_baseline(wl, w, b, args.cpu_budget)
+    model.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,22 @@
+"""P-EAGLE parallel-draft step on AMD MI355X (gfx950).
+
+Public API (thin ctypes binding over libpeagle.so; all work runs in HIP):
+
+* :class:`DraftModel` -- drafter shape + borrowed device weights
+* :func:`prepare_draft_batch` -- expand the verified batch, place hidden states
+* :func:`draft_forward` -- one drafter pass producing K tokens per sequence
+* :func:`accept` -- greedy accepted length and next bonus token
+"""
+
+from ._lib import (  # noqa: F401
+    DraftModel,
+    PeError,
+    accept,
+    draft_forward,
+    load,
+    prepare_draft_batch,
+    status_string,
+    PE_KERNEL_LM_HEAD,
+    PE_KERNEL_PREPARE,
+    PE_KERNEL_ATTENTION,
+)

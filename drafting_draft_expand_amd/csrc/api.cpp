@@ -1,0 +1,365 @@
+// C ABI of the parallel-draft step: host-side validation, workspace layout and
+// launch sequencing.  Declarations and argument contracts: include/peagle.h.
+#include "../../include/peagle.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <new>
+#include <utility>
+#include <vector>
+
+#include "internal.h"
+
+using pe::DType;
+
+namespace {
+
+struct Timing {
+  bool enabled = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> events;  // recorded pairs
+  size_t used = 0;
+};
+
+}  // namespace
+
+struct pe_model {
+  pe_model_desc d;
+  pe_weights w;
+  std::vector<pe_layer_weights> layers;
+  int num_cus = 0;  // queried on first launch
+  Timing timing[3];
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline DType dt(const pe_model* m) { return m->d.dtype == PE_F32 ? DType::F32 : DType::BF16; }
+
+int attention_splits(int c, int n_kv) {
+  const int base = c * n_kv;
+  int s = (512 + base - 1) / base;
+  if (s < 1) s = 1;
+  if (s > 64) s = 64;
+  return s;
+}
+
+// Workspace carve-up for one forward call.
+struct Workspace {
+  size_t x, act, qkv, q, attn_part, mlp, top2, f, total;
+  int splits, lm_parts;
+};
+
+Workspace plan_workspace(const pe_model* m, int c, int K, int N) {
+  const pe_model_desc& d = m->d;
+  const size_t eb = d.dtype == PE_F32 ? 4 : 2;
+  const int S = c * K;
+  const int H = d.hidden, qd = d.n_q * d.head_dim, kvd = d.n_kv * d.head_dim;
+  int act_cols = 2 * H;
+  if (qd > act_cols) act_cols = qd;
+  if (d.inter > act_cols) act_cols = d.inter;
+  Workspace w{};
+  w.splits = attention_splits(c, d.n_kv);
+  w.lm_parts = 4096;  // upper bound on LM-head workgroups (grid is capped at 2 per CU)
+  size_t off = 0;
+  w.x = off;         off += align_up(size_t(N) * H * 4);
+  w.act = off;       off += align_up(size_t(N) * act_cols * eb);
+  w.qkv = off;       off += align_up(size_t(N) * (qd + 2 * kvd) * 4);
+  w.q = off;         off += align_up(size_t(N) * qd * eb);
+  w.attn_part = off; off += align_up(size_t(N) * d.n_q * w.splits * (d.head_dim + 2) * 4);
+  w.mlp = off;       off += align_up(size_t(N) * d.inter * eb);
+  w.top2 = off;      off += align_up(size_t(S) * w.lm_parts * sizeof(pe::Top2));
+  w.f = off;         off += align_up(size_t(S) * H * eb);
+  w.total = off;
+  return w;
+}
+
+pe_status check_desc(const pe_model_desc* d) {
+  if (!d) return PE_EINVAL;
+  if (d->hidden <= 0 || d->hidden % 8 != 0) return PE_EUNSUPPORTED;
+  if (d->n_layers < 0 || d->block_size != 16) return PE_EUNSUPPORTED;
+  if (d->dtype != PE_F32 && d->dtype != PE_BF16) return PE_EUNSUPPORTED;
+  if (d->n_layers == 0) return PE_OK;  // expansion-only model
+  if (d->vocab <= 0 || d->n_q <= 0 || d->n_kv <= 0 || d->n_q % d->n_kv != 0) return PE_EINVAL;
+  if (d->head_dim != 16 && d->head_dim != 32 && d->head_dim != 64 && d->head_dim != 128)
+    return PE_EUNSUPPORTED;
+  if (d->inter <= 0 || d->inter % 8 != 0) return PE_EUNSUPPORTED;
+  if ((d->n_q * d->head_dim) % 8 != 0) return PE_EUNSUPPORTED;
+  if (d->mask_token_id < 0 || d->mask_token_id >= d->vocab) return PE_EINVAL;
+  if (!(d->rms_eps > 0.f) || !(d->rope_theta > 0.f)) return PE_EINVAL;
+  return PE_OK;
+}
+
+int num_cus(pe_model* m) {
+  if (m->num_cus > 0) return m->num_cus;
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+    m->num_cus = n;
+  else
+    m->num_cus = 256;
+  return m->num_cus;
+}
+
+// Optional event pair around one launch of a timed kernel class.
+struct TimedScope {
+  Timing* t;
+  hipStream_t s;
+  hipEvent_t stop = nullptr;
+  TimedScope(pe_model* m, pe_kernel_class k, hipStream_t stream) : t(&m->timing[k]), s(stream) {
+    if (!t->enabled) { t = nullptr; return; }
+    if (t->used == t->events.size()) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) { t = nullptr; return; }
+      t->events.emplace_back(a, b);
+    }
+    (void)hipEventRecord(t->events[t->used].first, s);
+    stop = t->events[t->used].second;
+  }
+  ~TimedScope() {
+    if (!t) return;
+    (void)hipEventRecord(stop, s);
+    ++t->used;
+  }
+};
+
+#define PE_HIP(expr)                                  \
+  do {                                                \
+    if ((expr) != hipSuccess) return PE_EHIP;          \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* pe_status_string(pe_status s) {
+  switch (s) {
+    case PE_OK: return "ok";
+    case PE_EINVAL: return "invalid argument";
+    case PE_EUNSUPPORTED: return "unsupported shape or dtype";
+    case PE_EWORKSPACE: return "workspace too small";
+    case PE_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+pe_status pe_model_create(const pe_model_desc* desc, const pe_weights* w, pe_model** out) {
+  if (!out || !w) return PE_EINVAL;
+  *out = nullptr;
+  pe_status st = check_desc(desc);
+  if (st != PE_OK) return st;
+  if (!w->h_shared || !aligned16(w->h_shared)) return PE_EINVAL;
+  if (desc->n_layers > 0) {
+    const void* req[] = {w->embed, w->w_fc, w->ln_f, w->w_lm};
+    for (const void* p : req)
+      if (!p || !aligned16(p)) return PE_EINVAL;
+    if (!w->layers) return PE_EINVAL;
+    for (int l = 0; l < desc->n_layers; ++l) {
+      const pe_layer_weights& L = w->layers[l];
+      const void* lp[] = {L.ln1, L.wq, L.wk, L.wv, L.wo, L.ln2, L.w_gate, L.w_up, L.w_down};
+      for (const void* p : lp)
+        if (!p || !aligned16(p)) return PE_EINVAL;
+    }
+  }
+  pe_model* m = new (std::nothrow) pe_model();
+  if (!m) return PE_EINVAL;
+  m->d = *desc;
+  m->w = *w;
+  if (desc->n_layers > 0) m->layers.assign(w->layers, w->layers + desc->n_layers);
+  m->w.layers = m->layers.empty() ? nullptr : m->layers.data();
+  *out = m;
+  return PE_OK;
+}
+
+void pe_model_destroy(pe_model* m) {
+  if (!m) return;
+  for (auto& t : m->timing)
+    for (auto& e : t.events) {
+      (void)hipEventDestroy(e.first);
+      (void)hipEventDestroy(e.second);
+    }
+  delete m;
+}
+
+size_t pe_workspace_bytes(const pe_model* m, int32_t c, int32_t K, int32_t N) {
+  if (!m || c <= 0 || K <= 0 || N <= 0 || m->d.n_layers <= 0) return 0;
+  return plan_workspace(m, c, K, N).total;
+}
+
+pe_status pe_prepare_draft_batch(const pe_model* m, int32_t c, int32_t K, int32_t T,
+                                 const int32_t* query_lens, const int32_t* target_ids,
+                                 const int32_t* target_pos, const int32_t* num_accepted,
+                                 const int32_t* bonus_ids, const void* target_hidden,
+                                 const int32_t* block_table, int32_t max_blocks, int32_t* draft_ids,
+                                 int32_t* draft_pos, int64_t* slot_mapping, uint8_t* is_rejected,
+                                 uint8_t* is_masked, int32_t* hidden_map, int32_t* cu_draft,
+                                 int32_t* kv_lens, int32_t* sample_idx, void* draft_hidden,
+                                 hipStream_t stream) {
+  if (!m || c <= 0 || K <= 0 || T < c || max_blocks <= 0) return PE_EINVAL;
+  const void* ptrs[] = {query_lens, target_ids, target_pos, num_accepted, bonus_ids, target_hidden,
+                        block_table, draft_ids, draft_pos, slot_mapping, is_rejected, is_masked,
+                        hidden_map, cu_draft, kv_lens, sample_idx, draft_hidden};
+  for (const void* p : ptrs)
+    if (!p) return PE_EINVAL;
+  if (!aligned16(target_hidden) || !aligned16(draft_hidden)) return PE_EINVAL;
+  const int64_t N = int64_t(T) + int64_t(c) * (K - 1);
+  if (N > INT32_MAX) return PE_EINVAL;
+  pe::PrepareArgs a{};
+  a.c = c; a.K = K; a.T = T; a.N = int(N); a.H = m->d.hidden;
+  a.block_size = m->d.block_size; a.max_blocks = max_blocks; a.mask_id = m->d.mask_token_id;
+  a.dtype = dt(m);
+  a.query_lens = query_lens; a.target_ids = target_ids; a.target_pos = target_pos;
+  a.num_accepted = num_accepted; a.bonus_ids = bonus_ids; a.block_table = block_table;
+  a.target_hidden = target_hidden; a.h_shared = m->w.h_shared;
+  a.draft_ids = draft_ids; a.draft_pos = draft_pos; a.slot_mapping = slot_mapping;
+  a.is_rejected = is_rejected; a.is_masked = is_masked; a.hidden_map = hidden_map;
+  a.cu_draft = cu_draft; a.kv_lens = kv_lens; a.sample_idx = sample_idx; a.draft_hidden = draft_hidden;
+  TimedScope ts(const_cast<pe_model*>(m), PE_KERNEL_PREPARE, stream);
+  PE_HIP(pe::launch_prepare(a, stream));
+  return PE_OK;
+}
+
+pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, const int32_t* draft_ids,
+                           const int32_t* draft_pos, const int64_t* slot_mapping,
+                           const uint8_t* is_rejected, const int32_t* cu_draft, const int32_t* kv_lens,
+                           const int32_t* sample_idx, const void* draft_hidden,
+                           const int32_t* block_table, int32_t max_blocks, void* const* k_cache,
+                           void* const* v_cache, void* workspace, size_t workspace_bytes,
+                           int32_t* draft_tokens, float* logits, float* top2_gap, hipStream_t stream) {
+  pe_model* m = const_cast<pe_model*>(mc);
+  if (!m || c <= 0 || K <= 0 || N < c * K || max_blocks <= 0) return PE_EINVAL;
+  if (m->d.n_layers <= 0) return PE_EUNSUPPORTED;
+  const void* ptrs[] = {draft_ids, draft_pos, slot_mapping, is_rejected, cu_draft, kv_lens,
+                        sample_idx, draft_hidden, block_table, k_cache, v_cache, workspace,
+                        draft_tokens};
+  for (const void* p : ptrs)
+    if (!p) return PE_EINVAL;
+  for (int l = 0; l < m->d.n_layers; ++l)
+    if (!k_cache[l] || !v_cache[l] || !aligned16(k_cache[l]) || !aligned16(v_cache[l])) return PE_EINVAL;
+  if (!aligned16(draft_hidden) || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return PE_EINVAL;
+  const Workspace ws = plan_workspace(m, c, K, N);
+  if (workspace_bytes < ws.total) return PE_EWORKSPACE;
+
+  const pe_model_desc& d = m->d;
+  const DType t = dt(m);
+  const int H = d.hidden, qd = d.n_q * d.head_dim, kvd = d.n_kv * d.head_dim, S = c * K;
+  char* wb = static_cast<char*>(workspace);
+  float* x = reinterpret_cast<float*>(wb + ws.x);
+  void* act = wb + ws.act;
+  float* qkv = reinterpret_cast<float*>(wb + ws.qkv);
+  void* qrot = wb + ws.q;
+  float* part = reinterpret_cast<float*>(wb + ws.attn_part);
+  void* mlp = wb + ws.mlp;
+  pe::Top2* top2 = reinterpret_cast<pe::Top2*>(wb + ws.top2);
+  void* f = wb + ws.f;
+  const int cus = num_cus(m);
+
+  // fc over [emb(id) ; h]
+  PE_HIP(pe::launch_build_fc_input(t, N, H, draft_ids, m->w.embed, draft_hidden, act, stream));
+  {
+    pe::GemvArgs g{};
+    g.M = N; g.Nout = H; g.K = 2 * H; g.x = act;
+    g.w_a = m->w.w_fc; g.n_a = H; g.w_b = g.w_c = m->w.w_fc; g.n_b = 0;
+    g.y = x; g.ldy = H;
+    PE_HIP(pe::launch_gemv(g, pe::Epi::Store, t, cus, stream));
+  }
+  for (int l = 0; l < d.n_layers; ++l) {
+    const pe_layer_weights& L = m->layers[l];
+    PE_HIP(pe::launch_rmsnorm(t, N, H, nullptr, x, L.ln1, d.rms_eps, act, stream));
+    {
+      pe::GemvArgs g{};
+      g.M = N; g.Nout = qd + 2 * kvd; g.K = H; g.x = act;
+      g.w_a = L.wq; g.n_a = qd; g.w_b = L.wk; g.n_b = kvd; g.w_c = L.wv;
+      g.y = qkv; g.ldy = qd + 2 * kvd;
+      PE_HIP(pe::launch_gemv(g, pe::Epi::Store, t, cus, stream));
+    }
+    {
+      pe::RopeArgs r{};
+      r.N = N; r.n_q = d.n_q; r.n_kv = d.n_kv; r.d = d.head_dim; r.block_size = d.block_size;
+      r.theta = d.rope_theta; r.dtype = t; r.qkv = qkv; r.pos = draft_pos; r.slot = slot_mapping;
+      r.rejected = is_rejected; r.q_out = qrot; r.k_cache = k_cache[l]; r.v_cache = v_cache[l];
+      PE_HIP(pe::launch_rope_kvwrite(r, stream));
+    }
+    {
+      pe::AttnArgs at{};
+      at.c = c; at.N = N; at.n_q = d.n_q; at.n_kv = d.n_kv; at.d = d.head_dim;
+      at.block_size = d.block_size; at.max_blocks = max_blocks; at.splits = ws.splits; at.dtype = t;
+      at.q = qrot; at.pos = draft_pos; at.rejected = is_rejected; at.cu_draft = cu_draft;
+      at.kv_lens = kv_lens; at.block_table = block_table; at.k_cache = k_cache[l];
+      at.v_cache = v_cache[l]; at.partial = part; at.out = act;
+      TimedScope ts(m, PE_KERNEL_ATTENTION, stream);
+      PE_HIP(pe::launch_attention(at, stream));
+    }
+    {
+      pe::GemvArgs g{};
+      g.M = N; g.Nout = H; g.K = qd; g.x = act;
+      g.w_a = g.w_b = g.w_c = L.wo; g.n_a = H; g.n_b = 0;
+      g.y = x; g.ldy = H;
+      PE_HIP(pe::launch_gemv(g, pe::Epi::AddTo, t, cus, stream));
+    }
+    PE_HIP(pe::launch_rmsnorm(t, N, H, nullptr, x, L.ln2, d.rms_eps, act, stream));
+    {
+      pe::GemvArgs g{};
+      g.M = N; g.Nout = d.inter; g.K = H; g.x = act;
+      g.w_a = L.w_gate; g.w_b = L.w_up; g.w_c = L.w_up; g.n_a = d.inter; g.n_b = d.inter;
+      g.y_op = mlp; g.ldy = d.inter;
+      PE_HIP(pe::launch_gemv(g, pe::Epi::SiluMul, t, cus, stream));
+    }
+    {
+      pe::GemvArgs g{};
+      g.M = N; g.Nout = H; g.K = d.inter; g.x = mlp;
+      g.w_a = g.w_b = g.w_c = L.w_down; g.n_a = H; g.n_b = 0;
+      g.y = x; g.ldy = H;
+      PE_HIP(pe::launch_gemv(g, pe::Epi::AddTo, t, cus, stream));
+    }
+  }
+  // final norm on the sampled rows, LM head + argmax
+  PE_HIP(pe::launch_rmsnorm(t, S, H, sample_idx, x, m->w.ln_f, d.rms_eps, f, stream));
+  {
+    pe::GemvArgs g{};
+    g.M = S; g.Nout = d.vocab; g.K = H; g.x = f;
+    g.w_a = g.w_b = g.w_c = m->w.w_lm; g.n_a = d.vocab; g.n_b = 0;
+    g.logits = logits; g.partials = top2;
+    if (pe::gemv_grid_x(S, d.vocab, pe::Epi::Argmax, t, cus) > ws.lm_parts) return PE_EUNSUPPORTED;
+    {
+      TimedScope ts(m, PE_KERNEL_LM_HEAD, stream);
+      PE_HIP(pe::launch_gemv(g, pe::Epi::Argmax, t, cus, stream));
+    }
+    PE_HIP(pe::launch_argmax_finalize(S, g.grid_x, top2, draft_tokens, top2_gap, stream));
+  }
+  return PE_OK;
+}
+
+pe_status pe_accept(int32_t c, int32_t K, const int32_t* draft, const int32_t* target, int32_t* acc,
+                    int32_t* bonus, hipStream_t stream) {
+  if (c <= 0 || K <= 0 || !draft || !target || !acc || !bonus) return PE_EINVAL;
+  PE_HIP(pe::launch_accept(c, K, draft, target, acc, bonus, stream));
+  return PE_OK;
+}
+
+pe_status pe_timing_enable(pe_model* m, pe_kernel_class k, int32_t enable) {
+  if (!m || k < PE_KERNEL_LM_HEAD || k > PE_KERNEL_ATTENTION) return PE_EINVAL;
+  m->timing[k].enabled = enable != 0;
+  m->timing[k].used = 0;
+  return PE_OK;
+}
+
+pe_status pe_timing_read(pe_model* m, pe_kernel_class k, double* total_ms, int64_t* launches) {
+  if (!m || !total_ms || !launches || k < PE_KERNEL_LM_HEAD || k > PE_KERNEL_ATTENTION) return PE_EINVAL;
+  Timing& t = m->timing[k];
+  double sum = 0.0;
+  for (size_t i = 0; i < t.used; ++i) {
+    PE_HIP(hipEventSynchronize(t.events[i].second));
+    float ms = 0.f;
+    PE_HIP(hipEventElapsedTime(&ms, t.events[i].first, t.events[i].second));
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = static_cast<int64_t>(t.used);
+  return PE_OK;
+}
+
+}  // extern "C"

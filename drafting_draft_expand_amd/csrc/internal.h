@@ -1,0 +1,96 @@
+// Host-side launch interfaces between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pe {
+
+enum class DType { F32 = 0, BF16 = 1 };
+
+// Best and runner-up logit over a set of vocabulary rows (ties -> lowest id).
+struct Top2 {
+  float v1;
+  int i1;
+  float v2;
+  int pad;
+};
+
+inline int elem_bytes(DType t) { return t == DType::F32 ? 4 : 2; }
+
+// ---------------------------------------------------------------- expansion
+struct PrepareArgs {
+  int c, K, T, N, H, block_size, max_blocks, mask_id;
+  DType dtype;
+  const int32_t *query_lens, *target_ids, *target_pos, *num_accepted, *bonus_ids, *block_table;
+  const void *target_hidden, *h_shared;
+  int32_t *draft_ids, *draft_pos;
+  int64_t *slot_mapping;
+  uint8_t *is_rejected, *is_masked;
+  int32_t *hidden_map, *cu_draft, *kv_lens, *sample_idx;
+  void *draft_hidden;
+};
+hipError_t launch_prepare(const PrepareArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- GEMV (skinny GEMM)
+enum class Epi { Store = 0, AddTo = 1, SiluMul = 2, Argmax = 3 };
+
+struct GemvArgs {
+  // Y[m, n] = sum_k X[m, k] * W[n, k] for m < M, n < Nout.
+  int M, Nout, K;
+  const void* x;          // operand rows [M, K], model dtype, row stride K
+  // W rows: [0, n_a) from w_a, [n_a, n_a + n_b) from w_b, the rest from w_c;
+  // every W row has K elements.  For Epi::SiluMul, w_a is the gate and w_b the
+  // up projection (both Nout rows).
+  const void *w_a, *w_b, *w_c;
+  int n_a, n_b;
+  // outputs
+  float* y;               // Store / AddTo: fp32 [M, ldy]
+  void* y_op;             // SiluMul: model dtype [M, ldy]
+  int ldy;
+  float* logits;          // Argmax: optional fp32 [M, Nout]
+  Top2* partials;         // Argmax: [M, gridDim.x]
+  int grid_x;             // filled by the launcher
+};
+hipError_t launch_gemv(GemvArgs& a, Epi epi, DType dt, int num_cus, hipStream_t s);
+int gemv_grid_x(int M, int Nout, Epi epi, DType dt, int num_cus);
+
+// ---------------------------------------------------------------- small kernels
+hipError_t launch_build_fc_input(DType dt, int N, int H, const int32_t* ids, const void* embed,
+                                 const void* draft_hidden, void* out, hipStream_t s);
+hipError_t launch_rmsnorm(DType dt, int rows, int H, const int32_t* row_idx, const float* x,
+                          const void* gain, float eps, void* out, hipStream_t s);
+
+struct RopeArgs {
+  int N, n_q, n_kv, d, block_size;
+  float theta;
+  DType dtype;
+  const float* qkv;             // [N, (n_q + 2 n_kv) d]
+  const int32_t* pos;
+  const int64_t* slot;
+  const uint8_t* rejected;
+  void* q_out;                  // [N, n_q d] model dtype
+  void *k_cache, *v_cache;      // [blocks, n_kv, block_size, d]
+};
+hipError_t launch_rope_kvwrite(const RopeArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  int c, N, n_q, n_kv, d, block_size, max_blocks, splits;
+  DType dtype;
+  const void* q;                // [N, n_q d] model dtype (rotated)
+  const int32_t* pos;
+  const uint8_t* rejected;
+  const int32_t *cu_draft, *kv_lens, *block_table;
+  const void *k_cache, *v_cache;
+  float* partial;               // [N, n_q, splits, d + 2]
+  void* out;                    // [N, n_q d] model dtype
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+hipError_t launch_argmax_finalize(int S, int parts, const Top2* partials, int32_t* tokens,
+                                  float* gap, hipStream_t s);
+hipError_t launch_accept(int c, int K, const int32_t* draft, const int32_t* target,
+                         int32_t* acc, int32_t* bonus, hipStream_t s);
+
+}  // namespace pe

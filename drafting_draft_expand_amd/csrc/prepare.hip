@@ -1,0 +1,126 @@
+// Batch expansion + hidden-state placement for one parallel-draft round.
+//
+// "P-EAGLE: Parallel Speculative Decoding in vLLM", vLLM Implementation
+// Details / Fused Triton Kernel: the draft batch differs in shape from the
+// verify batch because of the MASK placeholders, so ids, positions, the bonus
+// token, the MASK fill and the rejected/masked/hidden-map metadata are rebuilt
+// on the GPU in a single launch.  Same page, Hidden State Management, and the
+// listing in "P-EAGLE: Faster LLM Inference with Parallel Speculative Decoding
+// in vLLM", vLLM implementation details: target hidden rows move to their new
+// rows and the learned shared hidden state fills the MASK rows.  KV Cache and
+// CUDA Graphs: rejected rows get slot -1.
+//
+// One launch, grid (sequence, column chunk), 256 threads:
+//   * every block derives its sequence's first verified row with a block-wide
+//     reduction over the preceding query lengths (the exclusive scan of L);
+//   * column chunk 0 writes the per-row metadata of the sequence;
+//   * every block copies its column slice of all L+K-1 hidden rows of the
+//     sequence with 16-byte loads/stores, reading either the target row the
+//     draft row maps from or h_shared.  Each output row is written once, so
+//     placement and broadcast form a single gather with no ordering hazard.
+#include "common.h"
+
+namespace pe {
+namespace {
+
+__device__ __forceinline__ int block_prefix_sum(const int32_t* v, int n) {
+  __shared__ int part[4];
+  int s = 0;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) s += v[i];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+  __syncthreads();
+  const int total = part[0] + part[1] + part[2] + part[3];
+  return total;
+}
+
+__global__ __launch_bounds__(256) void prepare_kernel(PrepareArgs a, int row_bytes, int vecs_per_row,
+                                                      int vecs_per_chunk) {
+  const int i = blockIdx.x;
+  const int s = block_prefix_sum(a.query_lens, i);
+  const int K = a.K;
+  const int L = a.query_lens[i];
+  const int acc = a.num_accepted[i];
+  const int D = s + i * (K - 1);
+  const int rows = L + K - 1;
+
+  if (blockIdx.y == 0) {
+    const int bonus = a.bonus_ids[i];
+    const int base = a.target_pos[s + acc];
+    const int bs = a.block_size;
+    const int32_t* bt = a.block_table + static_cast<int64_t>(i) * a.max_blocks;
+    for (int r = threadIdx.x; r < rows; r += blockDim.x) {
+      int id, pos;
+      uint8_t masked = 0, rejected = 0;
+      if (r <= acc) {                       // accepted rows, then the bonus row
+        id = r < acc ? a.target_ids[s + r + 1] : bonus;
+        pos = a.target_pos[s + r];
+      } else if (r < acc + K) {             // K-1 parallel-drafting MASK rows
+        id = a.mask_id;
+        pos = base + (r - acc);
+        masked = 1;
+      } else {                              // rejected verified rows
+        const int j = r - (K - 1);
+        id = j + 1 < L ? a.target_ids[s + j + 1] : bonus;
+        pos = a.target_pos[s + j];
+        rejected = 1;
+      }
+      const int row = D + r;
+      a.draft_ids[row] = id;
+      a.draft_pos[row] = pos;
+      a.is_masked[row] = masked;
+      a.is_rejected[row] = rejected;
+      a.slot_mapping[row] =
+          rejected ? int64_t(-1) : int64_t(bt[pos / bs]) * bs + pos % bs;
+    }
+    for (int j = threadIdx.x; j < L; j += blockDim.x)
+      a.hidden_map[s + j] = j <= acc ? D + j : D + j + K - 1;
+    for (int k = threadIdx.x; k < K; k += blockDim.x) a.sample_idx[i * K + k] = D + acc + k;
+    if (threadIdx.x == 0) {
+      a.cu_draft[i] = D;
+      a.kv_lens[i] = base + K;
+      if (i == a.c - 1) a.cu_draft[a.c] = a.N;
+    }
+  }
+
+  // hidden placement: gather of 16-byte vectors for this block's column slice
+  const int v0 = blockIdx.y * vecs_per_chunk;
+  const int width = min(vecs_per_chunk, vecs_per_row - v0);
+  if (width <= 0) return;
+  const char* th = static_cast<const char*>(a.target_hidden);
+  const char* hs = static_cast<const char*>(a.h_shared);
+  char* out = static_cast<char*>(a.draft_hidden);
+  const int total = rows * width;
+  for (int f = threadIdx.x; f < total; f += blockDim.x) {
+    const int r = f / width;
+    const int v = v0 + f - r * width;
+    const char* src;
+    if (r > acc && r < acc + K) {
+      src = hs + v * 16;
+    } else {
+      const int j = r <= acc ? r : r - (K - 1);
+      src = th + static_cast<int64_t>(s + j) * row_bytes + v * 16;
+    }
+    store16(out + static_cast<int64_t>(D + r) * row_bytes + v * 16, load16(src));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prepare(const PrepareArgs& a, hipStream_t stream) {
+  const int row_bytes = a.H * elem_bytes(a.dtype);
+  const int vecs = row_bytes / 16;
+  // enough blocks to cover the chip even at concurrency 1
+  int chunks = (512 + a.c - 1) / a.c;
+  chunks = chunks < 1 ? 1 : chunks;
+  const int max_chunks = (vecs + 7) / 8;
+  if (chunks > max_chunks) chunks = max_chunks;
+  const int per_chunk = (vecs + chunks - 1) / chunks;
+  chunks = (vecs + per_chunk - 1) / per_chunk;
+  dim3 grid(a.c, chunks);
+  hipLaunchKernelGGL(prepare_kernel, grid, dim3(256), 0, stream, a, row_bytes, vecs, per_chunk);
+  return hipGetLastError();
+}
+
+}  // namespace pe

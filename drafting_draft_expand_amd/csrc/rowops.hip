@@ -1,0 +1,172 @@
+// Row-wise kernels of the drafter pass: fc input assembly, RMSNorm, RoPE with
+// the paged KV write, LM-head argmax merge and greedy acceptance.
+#include "common.h"
+
+namespace pe {
+namespace {
+
+// u[r] = [embed[ids[r]] ; draft_hidden[r]]  -- the concatenation of the
+// "P-EAGLE: Faster LLM Inference with Parallel Speculative Decoding in vLLM"
+// Input_i equation (token embedding first, hidden state second).
+__global__ __launch_bounds__(256) void fc_input_kernel(int H_bytes, const int32_t* ids, const char* embed,
+                                                       const char* hidden, char* out) {
+  const int r = blockIdx.x;
+  const int hv = H_bytes / 16;
+  const char* e = embed + static_cast<int64_t>(ids[r]) * H_bytes;
+  const char* h = hidden + static_cast<int64_t>(r) * H_bytes;
+  char* o = out + static_cast<int64_t>(r) * 2 * H_bytes;
+  for (int v = threadIdx.x; v < 2 * hv; v += blockDim.x) {
+    const char* src = v < hv ? e + v * 16 : h + (v - hv) * 16;
+    store16(o + v * 16, load16(src));
+  }
+}
+
+// out[i] = x[row] / sqrt(mean(x[row]^2) + eps) * gain, rounded to the operand
+// dtype; one wave per row, row = row_idx ? row_idx[i] : i.
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(int rows, int H, const int32_t* row_idx, const float* x,
+                                                      const T* gain, float eps, T* out) {
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= rows) return;
+  const int r = row_idx ? row_idx[i] : i;
+  const float* xr = x + static_cast<int64_t>(r) * H;
+  float ss = 0.f;
+  for (int k = lane * 4; k < H; k += 256) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(xr + k);
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+  ss = wave_sum(ss);
+  const float scale = 1.f / sqrtf(ss / static_cast<float>(H) + eps);
+  T* o = out + static_cast<int64_t>(i) * H;
+  for (int k = lane; k < H; k += 64) o[k] = Elem<T>::from_f32(xr[k] * scale * Elem<T>::to_f32(gain[k]));
+}
+
+// Rotate-half RoPE of q and k at the row's position, q stored as the attention
+// operand, k and v written to the paged cache at the row's slot.  Rows with
+// slot -1 (rejected, "P-EAGLE: Parallel Speculative Decoding in vLLM", KV Cache
+// and CUDA Graphs) write nothing.  Angles are formed in double precision so
+// that large positions keep full fp32 accuracy in cos/sin.
+template <typename T>
+__global__ __launch_bounds__(256) void rope_kv_kernel(RopeArgs a) {
+  const int r = blockIdx.x;
+  const int half = a.d / 2;
+  const int heads = a.n_q + 2 * a.n_kv;
+  const int p = blockIdx.y * blockDim.x + threadIdx.x;
+  if (p >= heads * half) return;
+  if (a.rejected[r]) return;
+  const int head = p / half;
+  const int j = p - head * half;
+  const float* src = a.qkv + static_cast<int64_t>(r) * heads * a.d + head * a.d;
+  float x1 = src[j], x2 = src[j + half];
+  if (head < a.n_q + a.n_kv) {
+    const double inv = pow(static_cast<double>(a.theta), -2.0 * j / a.d);
+    const double ang = static_cast<double>(a.pos[r]) * inv;
+    double sd, cd;
+    sincos(ang, &sd, &cd);
+    const float c = static_cast<float>(cd), s = static_cast<float>(sd);
+    const float y1 = x1 * c - x2 * s;
+    const float y2 = x2 * c + x1 * s;
+    x1 = y1;
+    x2 = y2;
+  }
+  if (head < a.n_q) {
+    T* q = static_cast<T*>(a.q_out) + static_cast<int64_t>(r) * a.n_q * a.d + head * a.d;
+    q[j] = Elem<T>::from_f32(x1);
+    q[j + half] = Elem<T>::from_f32(x2);
+    return;
+  }
+  const int64_t slot = a.slot[r];
+  if (slot < 0) return;
+  const bool is_k = head < a.n_q + a.n_kv;
+  const int g = is_k ? head - a.n_q : head - a.n_q - a.n_kv;
+  const int64_t blk = slot / a.block_size;
+  const int off = static_cast<int>(slot - blk * a.block_size);
+  T* dst = static_cast<T*>(is_k ? a.k_cache : a.v_cache) +
+           ((blk * a.n_kv + g) * a.block_size + off) * a.d;
+  dst[j] = Elem<T>::from_f32(x1);
+  dst[j + half] = Elem<T>::from_f32(x2);
+}
+
+// Merge the per-workgroup LM-head candidates of each sampled row: token =
+// best id (lowest id on ties), gap = best minus runner-up logit.
+__global__ __launch_bounds__(64) void argmax_finalize_kernel(int parts, const Top2* partials, int32_t* tokens,
+                                                             float* gap) {
+  const int s = blockIdx.x;
+  const int lane = threadIdx.x;
+  Top2 best = top2_empty();
+  for (int p = lane; p < parts; p += 64) best = top2_merge(best, partials[static_cast<int64_t>(s) * parts + p]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    Top2 o;
+    o.v1 = __shfl_xor(best.v1, off, 64);
+    o.i1 = __shfl_xor(best.i1, off, 64);
+    o.v2 = __shfl_xor(best.v2, off, 64);
+    o.pad = 0;
+    best = top2_merge(best, o);
+  }
+  if (lane == 0) {
+    tokens[s] = best.i1;
+    if (gap) gap[s] = best.v1 - best.v2;
+  }
+}
+
+// Greedy acceptance: longest prefix where draft == target, then the bonus
+// token ("P-EAGLE: Parallel Speculative Decoding in vLLM", Acceptance Length).
+__global__ __launch_bounds__(256) void accept_kernel(int c, int K, const int32_t* draft, const int32_t* target,
+                                                     int32_t* acc, int32_t* bonus) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= c) return;
+  const int32_t* d = draft + static_cast<int64_t>(i) * K;
+  const int32_t* t = target + static_cast<int64_t>(i) * (K + 1);
+  int n = 0;
+  while (n < K && d[n] == t[n]) ++n;
+  acc[i] = n;
+  bonus[i] = t[n];
+}
+
+}  // namespace
+
+hipError_t launch_build_fc_input(DType dt, int N, int H, const int32_t* ids, const void* embed,
+                                 const void* draft_hidden, void* out, hipStream_t s) {
+  hipLaunchKernelGGL(fc_input_kernel, dim3(N), dim3(256), 0, s, H * elem_bytes(dt), ids,
+                     static_cast<const char*>(embed), static_cast<const char*>(draft_hidden),
+                     static_cast<char*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(DType dt, int rows, int H, const int32_t* row_idx, const float* x, const void* gain,
+                          float eps, void* out, hipStream_t s) {
+  dim3 grid((rows + 3) / 4);
+  if (dt == DType::F32)
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, grid, dim3(256), 0, s, rows, H, row_idx, x,
+                       static_cast<const float*>(gain), eps, static_cast<float*>(out));
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, grid, dim3(256), 0, s, rows, H, row_idx, x,
+                       static_cast<const bf16_t*>(gain), eps, static_cast<bf16_t*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_kvwrite(const RopeArgs& a, hipStream_t s) {
+  const int pairs = (a.n_q + 2 * a.n_kv) * (a.d / 2);
+  dim3 grid(a.N, (pairs + 255) / 256);
+  if (a.dtype == DType::F32)
+    hipLaunchKernelGGL(rope_kv_kernel<float>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_finalize(int S, int parts, const Top2* partials, int32_t* tokens, float* gap,
+                                  hipStream_t s) {
+  hipLaunchKernelGGL(argmax_finalize_kernel, dim3(S), dim3(64), 0, s, parts, partials, tokens, gap);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept(int c, int K, const int32_t* draft, const int32_t* target, int32_t* acc,
+                         int32_t* bonus, hipStream_t s) {
+  hipLaunchKernelGGL(accept_kernel, dim3((c + 255) / 256), dim3(256), 0, s, c, K, draft, target, acc, bonus);
+  return hipGetLastError();
+}
+
+}  // namespace pe

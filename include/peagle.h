@@ -1,0 +1,211 @@
+/*
+ * peagle.h -- C ABI of the P-EAGLE parallel-draft step for AMD MI355X (gfx950).
+ *
+ * One parallel-draft round takes the batch the target model just verified and
+ * proposes K draft tokens per sequence with a single drafter pass:
+ *
+ *   pe_prepare_draft_batch  expand the verified batch into the draft layout and
+ *                           place the hidden states (target rows moved to their
+ *                           new rows, the learned shared hidden state broadcast
+ *                           into the MASK rows);
+ *   pe_draft_forward        fc(emb ++ h) -> decoder layer(s) over the paged KV
+ *                           cache -> LM head -> argmax, for all K drafts at once;
+ *   pe_accept               greedy accepted length against target tokens.
+ *
+ * Sources (page title, section):
+ *   [PF] "P-EAGLE: Faster LLM Inference with Parallel Speculative Decoding in
+ *        vLLM" -- how it works (Input_i equation); vLLM implementation details
+ *        (hidden-state placement listing).
+ *   [PP] "P-EAGLE: Parallel Speculative Decoding in vLLM" -- Step 2: Parallel
+ *        Drafting; vLLM Implementation Details: Fused Triton Kernel, Hidden
+ *        State Management, KV Cache and CUDA Graphs; Acceptance Length (AL).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument except the `pe_model_desc`, `pe_weights`,
+ *     `pe_layer_weights` structs and the host arrays of cache pointers is a
+ *     DEVICE pointer on the current HIP device, owned by the caller and
+ *     borrowed for the duration of the (asynchronous) work on `stream`.
+ *     The library never allocates or frees device memory; scratch space comes
+ *     from the caller's workspace.
+ *   - All work is enqueued on `stream`; the calls return before it finishes.
+ *   - Tensors are dense and row-major.  Floating-point tensors use the model
+ *     dtype (`PE_F32`: IEEE float32, `PE_BF16`: bfloat16 bit patterns) except
+ *     where stated.  Every tensor base pointer must be 16-byte aligned.
+ *   - Paged KV cache of a layer: [num_blocks, n_kv, block_size, head_dim] in the
+ *     model dtype; logical position p of sequence i lives at slot
+ *     block_table[i*max_blocks + p/block_size]*block_size + p%block_size.
+ *   - Errors: calls return a pe_status.  Misuse detectable on the host (null
+ *     pointer, non-positive sizes, unsupported shape, misaligned pointer, too
+ *     small workspace) returns PE_EINVAL / PE_EUNSUPPORTED / PE_EWORKSPACE
+ *     before anything is enqueued.  A failed launch returns PE_EHIP.  Values
+ *     held in device memory (token ids < vocab, 0 <= accepted <= L-1, block
+ *     tables covering every position a row occupies) are the caller's contract
+ *     and are not checked.
+ */
+#ifndef PEAGLE_H
+#define PEAGLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PE_OK = 0,
+  PE_EINVAL = -1,       /* bad argument (null pointer, size out of range, misaligned) */
+  PE_EUNSUPPORTED = -2, /* shape or dtype this build has no kernel for */
+  PE_EWORKSPACE = -3,   /* workspace smaller than pe_workspace_bytes() */
+  PE_EHIP = -4          /* a HIP launch or runtime call failed */
+} pe_status;
+
+typedef enum { PE_F32 = 0, PE_BF16 = 1 } pe_dtype;
+
+/* Drafter shape and constants (host memory, copied by pe_model_create).
+ * n_layers == 0 declares an expansion-only model: only h_shared is needed and
+ * only pe_prepare_draft_batch may be called with it. */
+typedef struct {
+  int32_t hidden;        /* H; H % 8 == 0 */
+  int32_t vocab;         /* V */
+  int32_t n_layers;      /* decoder layers, >= 0 */
+  int32_t n_q;           /* query heads */
+  int32_t n_kv;          /* kv heads, n_q % n_kv == 0 (q head h reads kv head h/(n_q/n_kv)) */
+  int32_t head_dim;      /* d in {16, 32, 64, 128} */
+  int32_t inter;         /* SwiGLU intermediate size I, I % 8 == 0 */
+  int32_t block_size;    /* KV page size in tokens; must be 16 */
+  float rms_eps;         /* RMSNorm epsilon */
+  float rope_theta;      /* rotary base; rotate-half pairs (j, j+d/2), angle p*theta^(-2j/d) */
+  int32_t mask_token_id; /* id written into MASK rows; emb(mask) = embed[mask_token_id] */
+  pe_dtype dtype;        /* storage/compute dtype of weights, hidden states and cache */
+} pe_model_desc;
+
+/* One pre-norm decoder layer (device pointers, row-major [out, in]). */
+typedef struct {
+  const void *ln1;    /* [H]            RMSNorm gain before attention */
+  const void *wq;     /* [n_q*d, H] */
+  const void *wk;     /* [n_kv*d, H] */
+  const void *wv;     /* [n_kv*d, H] */
+  const void *wo;     /* [H, n_q*d] */
+  const void *ln2;    /* [H]            RMSNorm gain before the MLP */
+  const void *w_gate; /* [I, H] */
+  const void *w_up;   /* [I, H] */
+  const void *w_down; /* [H, I] */
+} pe_layer_weights;
+
+/* Drafter weights (device pointers; `layers` is a HOST array of n_layers). */
+typedef struct {
+  const void *embed;    /* [V, H] token embeddings; row mask_token_id is emb(mask) */
+  const void *w_fc;     /* [H, 2H] fc over concat(emb(id), h) ([PF] Input_i) */
+  const void *ln_f;     /* [H] final RMSNorm gain */
+  const void *w_lm;     /* [V, H] LM head */
+  const void *h_shared; /* [H] learned shared hidden state for MASK rows ([PF], [PP] Hidden State Management) */
+  const pe_layer_weights *layers;
+} pe_weights;
+
+typedef struct pe_model pe_model; /* opaque, immutable after creation, usable from any stream */
+
+/* Validate the description and weight pointers and build a model handle
+ * (host memory only).  Returns PE_EINVAL / PE_EUNSUPPORTED on bad input. */
+pe_status pe_model_create(const pe_model_desc *desc, const pe_weights *weights, pe_model **out);
+void pe_model_destroy(pe_model *model);
+
+/* Bytes of workspace pe_draft_forward needs for a batch of `num_seqs`
+ * sequences, depth K and `num_rows` draft rows (0 on invalid input). */
+size_t pe_workspace_bytes(const pe_model *model, int32_t num_seqs, int32_t K, int32_t num_rows);
+
+/* Expand the verified batch into the draft batch.  [PP] Fused Triton Kernel:
+ * copy ids and positions, insert the bonus token, fill the K-1 parallel-drafting
+ * slots with the MASK id and emit the rejected/masked masks and the hidden-state
+ * map; [PP] KV Cache and CUDA Graphs: rejected rows get slot -1; [PF] vLLM
+ * implementation details / [PP] Hidden State Management: target hidden rows are
+ * moved to their mapped rows and h_shared is broadcast into the MASK rows.
+ *
+ * Inputs (c = num_seqs, T = total_target_rows = sum of query_lens):
+ *   query_lens[c]    L_i >= 1 verified rows of sequence i (rows are sequence-major)
+ *   target_ids[T]    token ids of the verified rows
+ *   target_pos[T]    positions of the verified rows (consecutive within a sequence)
+ *   num_accepted[c]  a_i, drafts accepted by the target, 0 <= a_i <= L_i-1
+ *   bonus_ids[c]     b_i, the token the target produced after the accepted ones
+ *   target_hidden[T,H]  target hidden state of every verified row
+ *   block_table[c,max_blocks]  physical page of each logical page
+ * Outputs (N = T + c*(K-1) draft rows; sequence i owns rows cu_draft[i]..cu_draft[i+1]-1):
+ *   draft_ids[N], draft_pos[N]   row r < a_i: token of verified row r+1 at the
+ *                                position of verified row r; row a_i: b_i (the
+ *                                first prediction row); rows a_i+1..a_i+K-1: MASK
+ *                                id at the next K-1 positions; then the L_i-1-a_i
+ *                                rejected verified rows (shifted ids, own positions)
+ *   slot_mapping[N]  cache slot of the row's position, -1 on rejected rows
+ *   is_rejected[N], is_masked[N]  0/1 bytes
+ *   hidden_map[T]    draft row that receives target row t
+ *   cu_draft[c+1]    first draft row of each sequence, cu_draft[c] = N
+ *   kv_lens[c]       cached positions after the pass: target_pos[first + a_i] + K
+ *   sample_idx[c*K]  the K rows whose logits give the drafts (first prediction row, MASK rows)
+ *   draft_hidden[N,H]  placed hidden states
+ */
+pe_status pe_prepare_draft_batch(const pe_model *model, int32_t num_seqs, int32_t K,
+                                 int32_t total_target_rows, const int32_t *query_lens,
+                                 const int32_t *target_ids, const int32_t *target_pos,
+                                 const int32_t *num_accepted, const int32_t *bonus_ids,
+                                 const void *target_hidden, const int32_t *block_table,
+                                 int32_t max_blocks, int32_t *draft_ids, int32_t *draft_pos,
+                                 int64_t *slot_mapping, uint8_t *is_rejected, uint8_t *is_masked,
+                                 int32_t *hidden_map, int32_t *cu_draft, int32_t *kv_lens,
+                                 int32_t *sample_idx, void *draft_hidden, hipStream_t stream);
+
+/* One drafter pass over every draft row, producing K tokens per sequence.
+ * [PF] how it works / [PP] Step 2: Parallel Drafting: all positions go through
+ * the layer(s) and the LM head together and t_1..t_K come out of one pass.
+ *
+ * Per row r: x = W_fc [embed[draft_ids[r]] ; draft_hidden[r]]; per layer:
+ * RMSNorm, q/k/v projections, rotate-half RoPE at draft_pos[r], (k, v) written
+ * to the layer's cache at slot_mapping[r] unless it is -1, grouped-query
+ * attention over positions 0..draft_pos[r] of the row's sequence (after all
+ * writes of the layer), output projection + residual, RMSNorm, SwiGLU MLP +
+ * residual; then RMSNorm and the LM head on the rows sample_idx[], greedy
+ * argmax (lowest id on ties).  Rejected rows are not computed.
+ *
+ *   metadata arrays: as produced by pe_prepare_draft_batch for the same batch
+ *   k_cache, v_cache: HOST arrays [n_layers] of device caches (read and written)
+ *   workspace: device scratch of at least pe_workspace_bytes(model, c, K, N)
+ *   draft_tokens[c*K]   int32 output, sequence-major
+ *   logits_or_null      optional float32 [c*K, V] logits of the sampled rows
+ *   top2_gap_or_null    optional float32 [c*K]: best minus second-best logit
+ */
+pe_status pe_draft_forward(const pe_model *model, int32_t num_seqs, int32_t K, int32_t num_rows,
+                           const int32_t *draft_ids, const int32_t *draft_pos,
+                           const int64_t *slot_mapping, const uint8_t *is_rejected,
+                           const int32_t *cu_draft, const int32_t *kv_lens,
+                           const int32_t *sample_idx, const void *draft_hidden,
+                           const int32_t *block_table, int32_t max_blocks,
+                           void *const *k_cache, void *const *v_cache, void *workspace,
+                           size_t workspace_bytes, int32_t *draft_tokens, float *logits_or_null,
+                           float *top2_gap_or_null, hipStream_t stream);
+
+/* Greedy acceptance ([PP] Acceptance Length (AL)): num_accepted[i] = length of
+ * the longest prefix on which draft_tokens[i*K..] equals target_tokens[i*(K+1)..],
+ * bonus_ids[i] = target_tokens[i*(K+1) + num_accepted[i]].
+ *   draft_tokens[c*K], target_tokens[c*(K+1)] int32 in; num_accepted[c], bonus_ids[c] int32 out. */
+pe_status pe_accept(int32_t num_seqs, int32_t K, const int32_t *draft_tokens,
+                    const int32_t *target_tokens, int32_t *num_accepted, int32_t *bonus_ids,
+                    hipStream_t stream);
+
+/* Static description of a status code. */
+const char *pe_status_string(pe_status status);
+
+/* Kernel timing for measurement harnesses.  While enabled for a kernel class,
+ * every launch of that class records a pair of HIP events on the stream it is
+ * launched on; pe_timing_read synchronizes on the recorded events and returns
+ * the summed elapsed milliseconds and the number of launches since enable.
+ * Not thread-safe against concurrent forward calls on the same model. */
+typedef enum { PE_KERNEL_LM_HEAD = 0, PE_KERNEL_PREPARE = 1, PE_KERNEL_ATTENTION = 2 } pe_kernel_class;
+pe_status pe_timing_enable(pe_model *model, pe_kernel_class kernel, int32_t enable);
+pe_status pe_timing_read(pe_model *model, pe_kernel_class kernel, double *total_ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PEAGLE_H */

@@ -19,6 +19,7 @@ from .workloads import (  # noqa: F401
     make_batch,
     make_agreement_draws,
     target_tokens_from_drafts,
+    store,
     f32_to_bf16_bits,
     bf16_bits_to_f32,
     NAN_BF16_BITS,

@@ -93,7 +93,8 @@ def _normal(shape, std: float, seed: int, tensor_id: int) -> np.ndarray:
     return out.reshape(shape)
 
 
-def _store(x: np.ndarray, dtype: str) -> np.ndarray:
+def store(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Encode float32 values in storage dtype ("fp32" or "bf16" bits)."""
     if dtype == "fp32":
         return np.ascontiguousarray(x, dtype=np.float32)
     if dtype == "bf16":
@@ -136,9 +137,14 @@ class Workload:
     accept_hi: int              # accepted drafts a_i ~ U{0..accept_hi}
     agree_p0: float = 0.7       # target agrees with draft d w.p. p0 * decay^d
     agree_decay: float = 1.0
-    seed: int = 0
+    seed: int = 0               # batch / cache / agreement draws
+    weight_seed: int = -1       # drafter weights (-1: same as seed); shared per drafter shape
     prep_only: bool = False     # batch expansion + hidden placement only
     description: str = ""
+
+    @property
+    def wseed(self) -> int:
+        return self.seed if self.weight_seed < 0 else self.weight_seed
 
     @property
     def L(self) -> int:
@@ -169,18 +175,18 @@ def _workloads() -> dict:
                     "c=64, K=7, contexts U{512..8192} in 16-token pages")
     w["gptoss20b-bf16-c1-k7"] = Workload(
         "gptoss20b-bf16-c1-k7", GPTOSS20B, c=1, K=7, ctx_lo=2048, ctx_hi=2048, accept_hi=7,
-        seed=2,
+        seed=2, weight_seed=2,
         description="GPT-OSS-20B-shaped drafter (H=2880, 64x64 q heads, 8 kv heads, I=7680, "
                     "V=201088), c=1, K=7, 2048 cached tokens")
     w["gptoss20b-bf16-c64-k7"] = Workload(
         "gptoss20b-bf16-c64-k7", GPTOSS20B, c=64, K=7, ctx_lo=512, ctx_hi=8192, accept_hi=7,
-        seed=3,
+        seed=3, weight_seed=2,
         description="GPT-OSS-20B-shaped drafter, c=64, K=7, contexts U{512..8192} paged")
     for k in (3, 5, 7):
         name = f"qwen3coder30b-bf16-c16-k{k}"
         w[name] = Workload(
             name, QWEN3CODER30B, c=16, K=k, ctx_lo=1024, ctx_hi=16384, accept_hi=k,
-            agree_p0=0.8, agree_decay=0.9, seed=4,
+            agree_p0=0.8, agree_decay=0.9, seed=4 + k, weight_seed=4,
             description=f"Qwen3-Coder-30B-shaped drafter (H=2048, 32x128 q heads, 4 kv heads, "
                         f"I=6144, V=151936), c=16, K={k}, contexts U{{1024..16384}} paged")
     return w
@@ -203,31 +209,31 @@ def make_weights(spec: ModelSpec, seed: int, prep_only: bool = False) -> dict:
     tid = iter(range(1, 10_000))
     w: dict = {}
     if prep_only:
-        w["h_shared"] = _store(_normal((H,), 1.0, seed, 9000), dt)
+        w["h_shared"] = store(_normal((H,), 1.0, seed, 9000), dt)
         return w
     emb = _normal((V, H), 0.02, seed, next(tid))
     emb[spec.mask_token_id] = _normal((H,), 1.0, seed, 9001)
-    w["embed"] = _store(emb, dt)
+    w["embed"] = store(emb, dt)
     del emb
-    w["w_fc"] = _store(_normal((H, 2 * H), 0.02, seed, next(tid)), dt)
+    w["w_fc"] = store(_normal((H, 2 * H), 0.02, seed, next(tid)), dt)
     layers = []
     for _ in range(spec.n_layers):
         lw = {
-            "ln1": _store(np.ones(H, np.float32), dt),
-            "wq": _store(_normal((spec.n_q * d, H), 0.02, seed, next(tid)), dt),
-            "wk": _store(_normal((spec.n_kv * d, H), 0.02, seed, next(tid)), dt),
-            "wv": _store(_normal((spec.n_kv * d, H), 0.02, seed, next(tid)), dt),
-            "wo": _store(_normal((H, spec.n_q * d), 0.02, seed, next(tid)), dt),
-            "ln2": _store(np.ones(H, np.float32), dt),
-            "w_gate": _store(_normal((spec.inter, H), 0.02, seed, next(tid)), dt),
-            "w_up": _store(_normal((spec.inter, H), 0.02, seed, next(tid)), dt),
-            "w_down": _store(_normal((H, spec.inter), 0.02, seed, next(tid)), dt),
+            "ln1": store(np.ones(H, np.float32), dt),
+            "wq": store(_normal((spec.n_q * d, H), 0.02, seed, next(tid)), dt),
+            "wk": store(_normal((spec.n_kv * d, H), 0.02, seed, next(tid)), dt),
+            "wv": store(_normal((spec.n_kv * d, H), 0.02, seed, next(tid)), dt),
+            "wo": store(_normal((H, spec.n_q * d), 0.02, seed, next(tid)), dt),
+            "ln2": store(np.ones(H, np.float32), dt),
+            "w_gate": store(_normal((spec.inter, H), 0.02, seed, next(tid)), dt),
+            "w_up": store(_normal((spec.inter, H), 0.02, seed, next(tid)), dt),
+            "w_down": store(_normal((H, spec.inter), 0.02, seed, next(tid)), dt),
         }
         layers.append(lw)
     w["layers"] = layers
-    w["ln_f"] = _store(np.ones(H, np.float32), dt)
-    w["w_lm"] = _store(_normal((V, H), 0.02, seed, next(tid)), dt)
-    w["h_shared"] = _store(_normal((H,), 1.0, seed, 9000), dt)
+    w["ln_f"] = store(np.ones(H, np.float32), dt)
+    w["w_lm"] = store(_normal((V, H), 0.02, seed, next(tid)), dt)
+    w["h_shared"] = store(_normal((H,), 1.0, seed, 9000), dt)
     return w
 
 
@@ -284,7 +290,7 @@ def make_batch(wl: Workload, seed: Optional[int] = None, with_cache: Optional[bo
     ids = rng.integers(0, spec.vocab - 1, size=T).astype(np.int32)   # MASK id never drawn
     bonus = rng.integers(0, spec.vocab - 1, size=c).astype(np.int32)
     pos = np.concatenate([P[i] + np.arange(L) for i in range(c)]).astype(np.int32)
-    hid = _store(_normal((T, spec.hidden), 1.0, seed, 7002), spec.dtype)
+    hid = store(_normal((T, spec.hidden), 1.0, seed, 7002), spec.dtype)
 
     bs = spec.block_size
     # blocks cover every position a draft row can occupy: P_i .. P_i + L + K - 2
@@ -308,7 +314,7 @@ def make_batch(wl: Workload, seed: Optional[int] = None, with_cache: Optional[bo
         for layer in range(spec.n_layers):
             pair = []
             for which in range(2):
-                x = _store(_normal(shape, 1.0, seed, 7100 + 2 * layer + which), spec.dtype)
+                x = store(_normal(shape, 1.0, seed, 7100 + 2 * layer + which), spec.dtype)
                 x[spare] = can
                 for i in range(c):
                     # positions >= P_i belong to this round's draft rows

@@ -1,0 +1,121 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects
+host-detectable misuse before touching the GPU (CPU only, no kernel launches)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "peagle.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pe_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from drafting_draft_expand_amd import _lib
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in peagle.h but not exported"
+
+
+def test_binding_names_match_abi():
+    import drafting_draft_expand_amd as pkg
+    for n in ("prepare_draft_batch", "draft_forward", "accept"):
+        assert callable(getattr(pkg, n))
+        assert f"pe_{n}" in _declared()
+
+
+def test_status_strings(lib):
+    from drafting_draft_expand_amd import _lib
+    assert _lib.status_string(0) == "ok"
+    assert _lib.status_string(-3) == "workspace too small"
+
+
+def _desc(**kw):
+    from drafting_draft_expand_amd import _lib
+    d = dict(hidden=64, vocab=512, n_layers=1, n_q=4, n_kv=2, head_dim=16, inter=128, block_size=16,
+             rms_eps=1e-6, rope_theta=1e4, mask_token_id=511, dtype=0)
+    d.update(kw)
+    return _lib.ModelDesc(**d)
+
+
+def _fake_weights():
+    from drafting_draft_expand_amd import _lib
+    p = 0x10000  # 16-byte aligned placeholders: create never dereferences them
+    layers = (_lib.LayerWeights * 1)(_lib.LayerWeights(*([p] * 9)))
+    w = _lib.Weights(p, p, p, p, p, ctypes.cast(layers, ctypes.POINTER(_lib.LayerWeights)))
+    return w, layers
+
+
+def _create(lib, desc):
+    w, keep = _fake_weights()
+    h = ctypes.c_void_p()
+    st = lib.pe_model_create(ctypes.byref(desc), ctypes.byref(w), ctypes.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(block_size=32), -2), (dict(head_dim=48), -2), (dict(hidden=60), -2), (dict(n_q=3), -1),
+    (dict(mask_token_id=512), -1), (dict(dtype=7), -2), (dict(rms_eps=0.0), -1), (dict(), 0),
+])
+def test_model_create_validation(lib, kw, expect):
+    st, h = _create(lib, _desc(**kw))
+    assert st == expect
+    if st == 0:
+        lib.pe_model_destroy(h)
+
+
+def test_calls_reject_bad_arguments_before_launch(lib):
+    st, h = _create(lib, _desc())
+    assert st == 0
+    try:
+        P = 0x20000
+        # c = 0 and null pointers
+        args = [h, 0, 3, 8] + [P] * 7 + [1] + [P] * 10 + [None]
+        assert lib.pe_prepare_draft_batch(*args) == -1
+        args = [h, 2, 3, 8] + [P] * 6 + [None] + [1] + [P] * 10 + [None]
+        assert lib.pe_prepare_draft_batch(*args) == -1
+        # misaligned hidden rows
+        args = [h, 2, 3, 8] + [P] * 5 + [P + 2] + [P] + [1] + [P] * 10 + [None]
+        assert lib.pe_prepare_draft_batch(*args) == -1
+        # workspace too small
+        need = lib.pe_workspace_bytes(h, 2, 3, 12)
+        assert need > 0
+        kp = (ctypes.c_void_p * 1)(P)
+        fargs = [h, 2, 3, 12] + [P] * 9 + [1, ctypes.cast(kp, ctypes.c_void_p), ctypes.cast(kp, ctypes.c_void_p),
+                                           0x40000, need - 1, P, None, None, None]
+        assert lib.pe_draft_forward(*fargs) == -3
+        # N inconsistent with c*K
+        fargs[3] = 5
+        assert lib.pe_draft_forward(*fargs) == -1
+        assert lib.pe_accept(0, 3, P, P, P, P, None) == -1
+        assert lib.pe_accept(2, 3, None, P, P, P, None) == -1
+        assert lib.pe_workspace_bytes(h, 0, 3, 12) == 0
+    finally:
+        lib.pe_model_destroy(h)
+
+
+def test_expansion_only_model_refuses_forward(lib):
+    from drafting_draft_expand_amd import _lib
+    d = _desc(n_layers=0)
+    w = _lib.Weights(None, None, None, None, 0x10000, None)
+    h = ctypes.c_void_p()
+    assert lib.pe_model_create(ctypes.byref(d), ctypes.byref(w), ctypes.byref(h)) == 0
+    P = 0x20000
+    kp = (ctypes.c_void_p * 1)(P)
+    fargs = [h, 2, 3, 12] + [P] * 9 + [1, ctypes.cast(kp, ctypes.c_void_p), ctypes.cast(kp, ctypes.c_void_p),
+                                       0x40000, 1 << 30, P, None, None, None]
+    assert lib.pe_draft_forward(*fargs) == -2
+    lib.pe_model_destroy(h)

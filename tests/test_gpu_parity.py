@@ -1,0 +1,204 @@
+"""GPU parity: the HIP path through the C ABI vs the CPU oracle, same inputs.
+
+Bars: integer outputs, masks, slot mappings, cache bytes outside the written
+slots and the placed hidden rows are bit-exact; logits within max-abs 1e-5
+(fp32 drafter) or 2e-2 (bf16 drafter); every draft token is an oracle argmax
+up to that tolerance; written KV entries match the oracle's rounded values.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth.device import from_torch, upload_batch
+from gpu_harness import (LOGIT_TOL, check_cache, check_prepare_exact, check_tokens, device_model, gpu_round,
+                         host_weights)
+from conftest import make_verified_batch
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _oracle_meta(spec, b):
+    return oracle.expand_batch(b.query_lens, b.target_ids, b.target_pos, b.num_accepted, b.bonus_ids,
+                               b.block_table, b.K, spec.mask_token_id, spec.block_size)
+
+
+# ----------------------------------------------------------------------------- expansion
+@pytest.mark.parametrize("name", ["tiny-fp32-c2-k3", "prep-bf16-c64-k7-h2880", "gptoss20b-bf16-c64-k7"])
+def test_prepare_bit_exact(name):
+    wl = synth.WORKLOADS[name]
+    _say(f"prepare {name}")
+    spec = wl.model
+    b = synth.make_batch(wl, with_cache=False)
+    w = host_weights(spec, wl.wseed, True)
+    model = device_model(spec, wl.wseed, True)
+    db = upload_batch(b, "cuda:0")
+    import drafting_draft_expand_amd as pe
+    prep = pe.prepare_draft_batch(model, wl.K, db["query_lens"], db["target_ids"], db["target_pos"],
+                                  db["num_accepted"], db["bonus_ids"], db["target_hidden"], db["block_table"])
+    torch.cuda.synchronize()
+    meta = _oracle_meta(spec, b)
+    hd = oracle.scatter_broadcast(b.target_hidden, meta["hidden_map"], meta["is_masked"], w["h_shared"], b.N)
+    check_prepare_exact(prep, meta, hd)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_prepare_sweep_bit_exact(dtype):
+    """Every (L, a) with L <= 8 at K in {1, 3, 7}, several sequences per batch."""
+    import drafting_draft_expand_amd as pe
+    spec = synth.ModelSpec(hidden=64, vocab=512, n_layers=0, n_q=1, n_kv=1, head_dim=16, inter=8, dtype=dtype)
+    rng = np.random.default_rng(7)
+    hs = synth.store(rng.standard_normal(64).astype(np.float32), dtype)
+    model = pe.DraftModel(64, 512, 0, 1, 1, 16, 8, dtype, {"h_shared": synth.device.to_torch(hs)})
+    for K in (1, 3, 7):
+        _say(f"prepare sweep dtype={dtype} K={K}")
+        Ls = [L for L in range(1, 9) for _ in range(L)]
+        As = [a for L in range(1, 9) for a in range(L)]
+        vb = make_verified_batch(rng, Ls, As, K, vocab=512, H=64)
+        th = synth.store(vb["target_hidden"], dtype)
+        t = lambda x: synth.device.to_torch(x)  # noqa: E731
+        prep = pe.prepare_draft_batch(model, K, t(vb["query_lens"]), t(vb["target_ids"]), t(vb["target_pos"]),
+                                      t(vb["num_accepted"]), t(vb["bonus_ids"]), t(th), t(vb["block_table"]))
+        torch.cuda.synchronize()
+        meta = oracle.expand_batch(vb["query_lens"], vb["target_ids"], vb["target_pos"], vb["num_accepted"],
+                                   vb["bonus_ids"], vb["block_table"], K, 511, 16)
+        hd = oracle.scatter_broadcast(th, meta["hidden_map"], meta["is_masked"], hs, len(meta["draft_ids"]))
+        check_prepare_exact(prep, meta, hd)
+
+
+# ----------------------------------------------------------------------------- forward
+def _forward_case(wl, seqs=None, batch=None, model_spec=None, wseed=None):
+    spec = model_spec or wl.model
+    wseed = wl.wseed if wseed is None else wseed
+    _say(f"forward {wl.name} seqs={seqs}")
+    w = host_weights(spec, wseed)
+    model = device_model(spec, wseed)
+    b = synth.make_batch(wl) if batch is None else batch
+    db = upload_batch(b, "cuda:0")
+    prep, tokens, logits, gap = gpu_round(model, db, b.K)
+    _say(f"  gpu done, oracle for seqs={seqs}")
+    ref = oracle.parallel_draft_step(spec, w, b, precision="mirror", seqs=seqs)
+    check_prepare_exact(prep, ref["meta"], ref["draft_hidden"])
+    fw = ref["forward"]
+    sel = fw["seqs"]
+    K = b.K
+    rows = np.concatenate([np.arange(i * K, (i + 1) * K) for i in sel])
+    g_logits = from_torch(logits)[rows]
+    o_logits = fw["logits"].reshape(len(rows), -1)
+    tol = LOGIT_TOL[spec.dtype]
+    err = np.max(np.abs(g_logits - o_logits))
+    _say(f"  max|dlogit| = {err:.3e} (tol {tol})")
+    assert np.isfinite(g_logits).all()
+    assert err <= tol
+    g_tok = from_torch(tokens).reshape(-1)[rows]
+    exact = check_tokens(g_tok, o_logits, tol)
+    _say(f"  tokens identical to oracle argmax: {exact:.3f}")
+    # gap reported by the GPU is consistent with its own logits
+    g_gap = from_torch(gap)[rows]
+    srt = np.sort(g_logits, axis=1)
+    np.testing.assert_allclose(g_gap, srt[:, -1] - srt[:, -2], rtol=0, atol=1e-6)
+    slots = from_torch(prep["slot_mapping"])
+    check_cache(spec, b.k_cache, b.v_cache, [from_torch(k) for k in db["k_cache"]],
+                [from_torch(v) for v in db["v_cache"]], slots, fw["cache_writes"], spec.dtype)
+    return dict(prep=prep, tokens=from_torch(tokens), oracle=ref, batch=b)
+
+
+def test_forward_tiny_fp32():
+    _forward_case(synth.WORKLOADS["tiny-fp32-c2-k3"])
+
+
+def test_forward_tiny_fp32_two_layers_ragged():
+    spec = synth.ModelSpec(hidden=96, vocab=300, n_layers=2, n_q=6, n_kv=2, head_dim=32, inter=160, dtype="fp32")
+    wl = synth.Workload("two-layer", spec, c=5, K=4, ctx_lo=0, ctx_hi=70, accept_hi=4, seed=12)
+    _forward_case(wl)
+
+
+@pytest.mark.parametrize("K", [1, 2, 5])
+def test_forward_depths_fp32(K):
+    spec = synth.TINY
+    wl = synth.Workload(f"tiny-k{K}", spec, c=3, K=K, ctx_lo=1, ctx_hi=40, accept_hi=K, seed=20 + K, weight_seed=0)
+    _forward_case(wl)
+
+
+def test_forward_prefill_like_fp32():
+    spec = synth.TINY
+    wl = synth.Workload("tiny-prefill", spec, c=3, K=3, ctx_lo=0, ctx_hi=20, accept_hi=3, seed=31, weight_seed=0)
+    b = synth.make_batch(wl, accepted=np.full(3, 3))
+    _forward_case(wl, batch=b)
+
+
+@pytest.mark.parametrize("dtype,d", [("fp32", 64), ("fp32", 128), ("bf16", 16), ("bf16", 32)])
+def test_forward_head_dims(dtype, d):
+    spec = synth.ModelSpec(hidden=128, vocab=700, n_layers=1, n_q=4, n_kv=2, head_dim=d, inter=256, dtype=dtype)
+    wl = synth.Workload(f"hd{d}-{dtype}", spec, c=3, K=4, ctx_lo=5, ctx_hi=150, accept_hi=4, seed=50 + d)
+    _forward_case(wl)
+
+
+def test_forward_small_bf16():
+    spec = synth.ModelSpec(hidden=256, vocab=1000, n_layers=1, n_q=8, n_kv=2, head_dim=64, inter=512)
+    wl = synth.Workload("small-bf16", spec, c=6, K=5, ctx_lo=10, ctx_hi=300, accept_hi=5, seed=41)
+    _forward_case(wl)
+
+
+def test_forward_gptoss_c1_full():
+    _forward_case(synth.WORKLOADS["gptoss20b-bf16-c1-k7"])
+
+
+def test_forward_gptoss_c64_sampled():
+    wl = synth.WORKLOADS["gptoss20b-bf16-c64-k7"]
+    b = synth.make_batch(wl)
+    a = b.num_accepted
+    pick = sorted({int(np.argmin(a)), int(np.argmax(a)), int(np.argmax(b.context)), 0, wl.c - 1})
+    _forward_case(wl, seqs=pick, batch=b)
+
+
+@pytest.mark.parametrize("K", [3, 5, 7])
+def test_forward_qwen_c16_sampled(K):
+    wl = synth.WORKLOADS[f"qwen3coder30b-bf16-c16-k{K}"]
+    b = synth.make_batch(wl)
+    pick = sorted({int(np.argmax(b.context)), int(np.argmin(b.num_accepted)), 15})
+    _forward_case(wl, seqs=pick, batch=b)
+
+
+# ----------------------------------------------------------------------------- acceptance
+@pytest.mark.parametrize("name", ["tiny-fp32-c2-k3", "qwen3coder30b-bf16-c16-k7"])
+def test_accept_matches_oracle(name):
+    import drafting_draft_expand_amd as pe
+    wl = synth.WORKLOADS[name]
+    rng = np.random.default_rng(3)
+    for trial in range(4):
+        c = [1, wl.c, 64, 1000][trial]
+        drafts = rng.integers(0, 50, size=(c, wl.K)).astype(np.int32)
+        u = rng.random((c, wl.K))
+        alt = rng.integers(0, wl.model.vocab - 2, size=(c, wl.K + 1))
+        tgt = synth.target_tokens_from_drafts(drafts, u, alt, wl.agree_probs(), wl.model.vocab)
+        acc, bonus = pe.accept(synth.device.to_torch(drafts), synth.device.to_torch(tgt))
+        torch.cuda.synchronize()
+        oa, ob = oracle.accept(drafts, tgt)
+        assert np.array_equal(from_torch(acc), oa) and np.array_equal(from_torch(bonus), ob)
+
+
+def test_round_trip_accept_on_gpu_drafts():
+    """Drafts from the GPU pass, targets from the synthetic agreement process:
+    GPU acceptance equals the oracle's on the same arrays."""
+    import drafting_draft_expand_amd as pe
+    wl = synth.WORKLOADS["tiny-fp32-c2-k3"]
+    model = device_model(wl.model, wl.wseed)
+    b = synth.make_batch(wl)
+    db = upload_batch(b, "cuda:0")
+    _, tokens, _, _ = gpu_round(model, db, b.K, want_logits=False)
+    u, alt = synth.make_agreement_draws(wl)
+    tgt = synth.target_tokens_from_drafts(from_torch(tokens), u, alt, wl.agree_probs(), wl.model.vocab)
+    acc, bonus = pe.accept(tokens, synth.device.to_torch(tgt))
+    torch.cuda.synchronize()
+    oa, ob = oracle.accept(from_torch(tokens), tgt)
+    assert np.array_equal(from_torch(acc), oa) and np.array_equal(from_torch(bonus), ob)
