@@ -39,11 +39,13 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline DType dt(const pe_model* m) { return m->d.dtype == PE_F32 ? DType::F32 : DType::BF16; }
 
+// KV-range splits per (sequence, kv head): enough workgroups to cover the
+// chip at low concurrency without multiplying the partial-result traffic.
 int attention_splits(int c, int n_kv) {
   const int base = c * n_kv;
-  int s = (512 + base - 1) / base;
+  int s = (128 + base - 1) / base;
   if (s < 1) s = 1;
-  if (s > 64) s = 64;
+  if (s > 32) s = 32;
   return s;
 }
 
@@ -246,6 +248,12 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
   const pe_model_desc& d = m->d;
   const DType t = dt(m);
   const int H = d.hidden, qd = d.n_q * d.head_dim, kvd = d.n_kv * d.head_dim, S = c * K;
+  {
+    // every projection's activation slice must fit the kernel's LDS budget
+    const int shapes[][2] = {{N, 2 * H}, {N, H}, {N, qd}, {N, d.inter}, {S, H}};
+    for (const auto& sh : shapes)
+      if (pe::gemv_lds_bytes(sh[0], sh[1], t) > 160 * 1024) return PE_EUNSUPPORTED;
+  }
   char* wb = static_cast<char*>(workspace);
   float* x = reinterpret_cast<float*>(wb + ws.x);
   void* act = wb + ws.act;
@@ -323,7 +331,7 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
     g.M = S; g.Nout = d.vocab; g.K = H; g.x = f;
     g.w_a = g.w_b = g.w_c = m->w.w_lm; g.n_a = d.vocab; g.n_b = 0;
     g.logits = logits; g.partials = top2;
-    if (pe::gemv_grid_x(S, d.vocab, pe::Epi::Argmax, t, cus) > ws.lm_parts) return PE_EUNSUPPORTED;
+    if (pe::gemv_grid_x(S, d.vocab, pe::Epi::Argmax, t, cus, H) > ws.lm_parts) return PE_EUNSUPPORTED;
     {
       TimedScope ts(m, PE_KERNEL_LM_HEAD, stream);
       PE_HIP(pe::launch_gemv(g, pe::Epi::Argmax, t, cus, stream));

@@ -141,46 +141,206 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
   }
 }
 
-// out[row, h, :] = sum_s acc_s * e^{m_s - M} / sum_s l_s * e^{m_s - M}
-template <typename T>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  const int row = blockIdx.x;
-  const int D = a.d;
-  T* out = static_cast<T*>(a.out) + static_cast<int64_t>(row) * a.n_q * D;
-  const bool rej = a.rejected[row];
-  for (int e = threadIdx.x; e < a.n_q * D; e += blockDim.x) {
-    const int h = e / D, dd = e - h * D;
-    float res = 0.f;
-    if (!rej) {
-      const float* p = a.partial + (static_cast<int64_t>(row) * a.n_q + h) * a.splits * (D + 2);
-      float M = -INFINITY;
-      for (int s = 0; s < a.splits; ++s) M = fmaxf(M, p[s * (D + 2) + D]);
-      float num = 0.f, den = 0.f;
-      for (int s = 0; s < a.splits; ++s) {
-        const float ms = p[s * (D + 2) + D];
-        if (ms == -INFINITY) continue;
-        const float w = expf(ms - M);
-        num = fmaf(p[s * (D + 2) + dd], w, num);
-        den = fmaf(p[s * (D + 2) + D + 1], w, den);
+// bf16, head_dim 64/128: the same split-KV attention on MFMA.
+//
+// A workgroup of 8 waves owns up to 128 queries (16 per wave) of one
+// (sequence, kv head, split).  Per 32-key tile the waves share K (row-major)
+// and V (transposed) in LDS.  Scores are formed transposed, S^T = K Q^T with
+// v_mfma_f32_16x16x32_bf16 (keys are the A rows, the wave's queries the B
+// columns), so each lane owns one query column: the online-softmax row
+// statistics need only the 4 lanes that share that column, and the
+// probabilities are already in the B-operand layout of O^T += V^T P^T.  The
+// MFMA's 32 k-slots of that product enumerate keys 4j..4j+3 and 16+4j..16+4j+3
+// for lane group j, the order in which the score tiles hold them.  The next
+// tile's K/V pieces are fetched into registers while the current one is used.
+template <int D>
+__global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
+  constexpr int KT = 32;
+  constexpr int KP = D + 8;    // padded K row (elements)
+  constexpr int VP = KT + 8;   // padded V^T row (elements)
+  constexpr int DT = D / 16;   // O^T tiles
+  constexpr int KK = D / 32;   // k-steps of S^T
+  constexpr int PER = KT * D / 8 / 512 > 0 ? KT * D / 8 / 512 : 1;  // 16-byte pieces per thread
+  __shared__ bf16_t ks[KT * KP];
+  __shared__ bf16_t vt[D * VP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, j = lane >> 4;
+  const int sp = blockIdx.x, g = blockIdx.y, i = blockIdx.z;
+  const int grp = a.n_q / a.n_kv;
+  const int r0 = a.cu_draft[i], r1 = a.cu_draft[i + 1];
+  const int kvlen = a.kv_lens[i];
+  const int chunk = ((kvlen + a.splits - 1) / a.splits + KT - 1) / KT * KT;
+  const int kb = sp * chunk;
+  const int ke = min(kvlen, kb + chunk);
+  const int nqry = (r1 - r0) * grp;
+  const float sl2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));  // scale * log2(e)
+  const bf16_t* qin = static_cast<const bf16_t*>(a.q);
+  const bf16_t* kc = static_cast<const bf16_t*>(a.k_cache);
+  const bf16_t* vc = static_cast<const bf16_t*>(a.v_cache);
+  const int32_t* bt = a.block_table + static_cast<int64_t>(i) * a.max_blocks;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const bool loader = tid < KT * D / 8;
+
+  for (int qb = 0; qb < nqry; qb += 128) {
+    const int qn = qb + wave * 16 + (lane & 15);
+    const int row = r0 + qn / grp;
+    const int h = g * grp + qn % grp;
+    const bool active = qn < nqry && !a.rejected[row];
+    const int qpos = active ? a.pos[row] : -1;
+    u32x4 qf[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qf[kk] = active ? load16(qin + (static_cast<int64_t>(row) * a.n_q + h) * D + 32 * kk + 8 * j) : zero;
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 o[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // register prefetch of one K/V tile: thread -> (key, 8-element column piece)
+    auto fetch = [&](int kt0, u32x4& kv, u32x4& vv) {
+      kv = zero;
+      vv = zero;
+      if (!loader) return;
+      const int key = tid / (D / 8), c8 = tid % (D / 8);
+      const int p = kt0 + key;
+      if (p < ke) {
+        const int64_t blk = bt[p / a.block_size];
+        const int64_t off = ((blk * a.n_kv + g) * a.block_size + p % a.block_size) * D + c8 * 8;
+        kv = load16(kc + off);
+        vv = load16(vc + off);
       }
-      res = num / den;
+    };
+    u32x4 kn, vn;
+    static_assert(PER == 1, "one 16-byte K and V piece per loader thread");
+    fetch(kb, kn, vn);
+    for (int kt0 = kb; kt0 < ke; kt0 += KT) {
+      __syncthreads();
+      if (loader) {
+        const int key = tid / (D / 8), c8 = tid % (D / 8);
+        store16(ks + key * KP + c8 * 8, kn);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w = vn[e];
+          vt[(c8 * 8 + 2 * e) * VP + key] = static_cast<bf16_t>(w & 0xffffu);
+          vt[(c8 * 8 + 2 * e + 1) * VP + key] = static_cast<bf16_t>(w >> 16);
+        }
+      }
+      __syncthreads();
+      if (kt0 + KT < ke) fetch(kt0 + KT, kn, vn);
+
+      // S^T for keys [0,16) and [16,32) of the tile
+      f32x4 st[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const u32x4 af = *reinterpret_cast<const u32x4*>(ks + (mt * 16 + (lane & 15)) * KP + 32 * kk + 8 * j);
+          st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af),
+                                                           __builtin_bit_cast(bf16x8, qf[kk]), st[mt], 0, 0, 0);
+        }
+      }
+      float sv[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int p = kt0 + mt * 16 + 4 * j + q;
+          const float s = (p < ke && p <= qpos) ? st[mt][q] * sl2 : -INFINITY;
+          sv[mt * 4 + q] = s;
+          mx = fmaxf(mx, s);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float corr = m_run == -INFINITY ? (m_new == -INFINITY ? 1.f : 0.f) : exp2f(m_run - m_new);
+      float rs = 0.f;
+      uint32_t pk[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = sv[2 * e] == -INFINITY ? 0.f : exp2f(sv[2 * e] - m_new);
+        const float p1 = sv[2 * e + 1] == -INFINITY ? 0.f : exp2f(sv[2 * e + 1] - m_new);
+        rs += p0 + p1;
+        pk[e] = static_cast<uint32_t>(f32_to_bf16(p0)) | (static_cast<uint32_t>(f32_to_bf16(p1)) << 16);
+      }
+      rs += __shfl_xor(rs, 16, 64);
+      rs += __shfl_xor(rs, 32, 64);
+      l_run = l_run * corr + rs;
+      m_run = m_new;
+      const u32x4 pb = {pk[0], pk[1], pk[2], pk[3]};
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        o[t] *= corr;
+        const bf16_t* vr = vt + (t * 16 + (lane & 15)) * VP;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vr + 4 * j);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16 + 4 * j);
+        const u32x4 af = {lo.x, lo.y, hi.x, hi.y};
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af),
+                                                       __builtin_bit_cast(bf16x8, pb), o[t], 0, 0, 0);
+      }
     }
-    out[e] = Elem<T>::from_f32(res);
+    if (qn < nqry) {
+      float* out = a.partial + ((static_cast<int64_t>(row) * a.n_q + h) * a.splits + sp) * (D + 2);
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out[t * 16 + 4 * j + q] = o[t][q];
+      if (j == 0) {
+        // row statistics in natural-log units for the combine step
+        out[D] = m_run == -INFINITY ? -INFINITY : m_run * 0.6931471805599453f;
+        out[D + 1] = l_run;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// out[row, h, :] = sum_s acc_s * e^{m_s - M} / sum_s l_s * e^{m_s - M};
+// one 64-thread workgroup per (row, head), split weights shared through LDS.
+template <typename T>
+__global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
+  __shared__ float wgt[64];
+  const int row = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int D = a.d, S = a.splits;
+  T* out = static_cast<T*>(a.out) + (static_cast<int64_t>(row) * a.n_q + h) * D;
+  if (a.rejected[row]) {
+    for (int dd = lane; dd < D; dd += 64) out[dd] = Elem<T>::from_f32(0.f);
+    return;
+  }
+  const float* p = a.partial + (static_cast<int64_t>(row) * a.n_q + h) * S * (D + 2);
+  const float ms = lane < S ? p[lane * (D + 2) + D] : -INFINITY;
+  const float M = wave_max(ms);
+  const float w = ms == -INFINITY ? 0.f : expf(ms - M);
+  const float den = wave_sum(lane < S ? w * p[lane * (D + 2) + D + 1] : 0.f);
+  wgt[lane] = w;
+  __syncthreads();
+  const float inv = 1.f / den;
+  for (int dd = lane; dd < D; dd += 64) {
+    float num = 0.f;
+    for (int s = 0; s < S; ++s) num = fmaf(p[s * (D + 2) + dd], wgt[s], num);
+    out[dd] = Elem<T>::from_f32(num * inv);
   }
 }
 
 template <typename T>
 hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.splits, a.n_kv, a.c);
-  switch (a.d) {
-    case 16: hipLaunchKernelGGL((attn_split_kernel<T, 16>), grid, dim3(256), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((attn_split_kernel<T, 32>), grid, dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((attn_split_kernel<T, 64>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((attn_split_kernel<T, 128>), grid, dim3(256), 0, s, a); break;
+  if (sizeof(T) == 2 && (a.d == 64 || a.d == 128)) {
+    if (a.d == 64)
+      hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, dim3(512), 0, s, a);
+  } else {
+    switch (a.d) {
+      case 16: hipLaunchKernelGGL((attn_split_kernel<T, 16>), grid, dim3(256), 0, s, a); break;
+      case 32: hipLaunchKernelGGL((attn_split_kernel<T, 32>), grid, dim3(256), 0, s, a); break;
+      case 64: hipLaunchKernelGGL((attn_split_kernel<T, 64>), grid, dim3(256), 0, s, a); break;
+      default: hipLaunchKernelGGL((attn_split_kernel<T, 128>), grid, dim3(256), 0, s, a); break;
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel<T>, dim3(a.N), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_combine_kernel<T>, dim3(a.N, a.n_q), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

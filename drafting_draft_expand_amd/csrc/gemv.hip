@@ -1,18 +1,25 @@
-// Weight-streaming skinny GEMM ("GEMV") for the drafter's projections.
+// Weight-streaming projections for few activation rows.
 //
-// Y[m, n] = sum_k X[m, k] * W[n, k] with few activation rows (M <= 16 per
-// launch slice).  The weights dominate the bytes, so the kernel is built
-// around streaming W once from HBM at full width:
-//   * each wave owns R consecutive output rows at a time; every lane loads
-//     16-byte slices of those R weight rows (non-temporal, they are read once)
-//     at k-vectors lane, lane+64, ... and the matching 16-byte slices of the
-//     MT activation rows, which stay hot in the caches;
-//   * products are accumulated in fp32 (v_dot2_f32_bf16 for bf16 weights);
-//   * the R*MT per-lane partial sums are folded across the wave with a
-//     reduce-scatter, so each lane ends with one finished dot product and
-//     applies the epilogue to it;
-//   * the grid is persistent-style (a few workgroups per CU, grid-stride over
-//     row groups), and rows of M beyond MT are handled by blockIdx.y slices.
+// Y[m, n] = sum_k X[m, k] * W[n, k] where the weights dominate the bytes, so
+// both kernels are organised around reading W exactly once from HBM with
+// 16-byte non-temporal loads and enough of them in flight per CU:
+//
+// gemv_lds_kernel (M <= 8 per slice, and every fp32 model):
+//   the activation slice is staged once per workgroup in LDS; each wave owns R
+//   consecutive output rows, every lane streams 16-byte pieces of those rows
+//   (two k-steps in flight) and multiplies them with the matching LDS piece of
+//   each activation row (v_dot2_f32_bf16 for bf16).  The R*MT per-lane partial
+//   sums are folded across the wave with a reduce-scatter, so every lane ends
+//   with one finished dot product and applies the epilogue to it.
+//
+// mfma_skinny_kernel (bf16, 8 < M <= 16 per slice):
+//   at 14-16 rows the VALU would be near saturation at full HBM rate, so the
+//   products run on v_mfma_f32_16x16x32_bf16: the activation rows are the A
+//   operand (one 16-byte piece per lane per k-step, read through the caches)
+//   and 16 weight rows are the B operand, loaded straight from HBM in the MFMA
+//   lane layout.  The SK waves of a workgroup split K, their partial tiles are
+//   summed through LDS and wave 0 applies the epilogue.
+//
 // Epilogues: plain store, residual add, SiLU(gate)*up of paired gate/up rows,
 // and the LM-head argmax, which keeps a running best/runner-up per activation
 // row and writes one candidate per workgroup for a final merge.
@@ -21,20 +28,29 @@
 namespace pe {
 namespace {
 
+// ------------------------------------------------------------------ VALU / LDS
 template <typename TW, int MT, int R, Epi EPI>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
+__global__ __launch_bounds__(256) void gemv_lds_kernel(GemvArgs a) {
   constexpr int VE = Elem<TW>::kVec;
   constexpr int NV = R * MT;
   constexpr int SH = 6 - Log2<NV>::value;
   constexpr int RG = (EPI == Epi::SiluMul) ? R / 2 : R;  // output rows per group
+  extern __shared__ u32x4 xs[];                            // [MT][K / VE]
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int K = a.K;
   const int KV = K / VE;
   const int m0 = blockIdx.y * MT;
   const int mcount = min(MT, a.M - m0);
-  const int64_t xrow = static_cast<int64_t>(K) * sizeof(TW);
-  const char* xb = static_cast<const char*>(a.x) + m0 * xrow;
+  {
+    const char* xb = static_cast<const char*>(a.x) + static_cast<int64_t>(m0) * K * sizeof(TW);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    for (int v = threadIdx.x; v < MT * KV; v += blockDim.x) {
+      const int m = v / KV;
+      xs[v] = m < mcount ? load16(xb + static_cast<int64_t>(v) * 16) : zero;
+    }
+    __syncthreads();
+  }
   const int G = (a.Nout + RG - 1) / RG;
   const int idx = lane >> SH;
   const int my_r = idx / MT;
@@ -63,16 +79,23 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     float acc[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) acc[i] = 0.f;
-    for (int j = lane; j < KV; j += 64) {
-      u32x4 w[R];
+    for (int j = lane; j < KV; j += 128) {
+      const bool two = j + 64 < KV;
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      u32x4 w0[R], w1[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) w[r] = load16_stream(wp[r] + j * VE);
+      for (int r = 0; r < R; ++r) w0[r] = load16_stream(wp[r] + j * VE);
+#pragma unroll
+      for (int r = 0; r < R; ++r) w1[r] = two ? load16_stream(wp[r] + (j + 64) * VE) : zero;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const int mm = m < mcount ? m : mcount - 1;
-        const u32x4 x = load16(xb + mm * xrow + j * 16);
+        const u32x4 x0 = xs[m * KV + j];
+        const u32x4 x1 = two ? xs[m * KV + j + 64] : zero;
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r * MT + m] = dot16<TW>(w[r], x, acc[r * MT + m]);
+        for (int r = 0; r < R; ++r) {
+          acc[r * MT + m] = dot16<TW>(w0[r], x0, acc[r * MT + m]);
+          acc[r * MT + m] = dot16<TW>(w1[r], x1, acc[r * MT + m]);
+        }
       }
     }
     const float val = wave_reduce_scatter<NV>(acc, lane);
@@ -87,8 +110,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
       const float up = __shfl(val, ((idx + RG * MT) << SH) & 63, 64);
       if (owner && my_r < RG && n < a.Nout && my_m < mcount) {
         const float s = val / (1.f + expf(-val));
-        static_cast<TW*>(a.y_op)[static_cast<int64_t>(m0 + my_m) * a.ldy + n] =
-            Elem<TW>::from_f32(s * up);
+        static_cast<TW*>(a.y_op)[static_cast<int64_t>(m0 + my_m) * a.ldy + n] = Elem<TW>::from_f32(s * up);
       }
     } else {  // Argmax
       if (owner && n < a.Nout && my_m < mcount) {
@@ -121,27 +143,177 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ MFMA skinny
+template <int SK, int U, Epi EPI>
+__global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
+  constexpr int NB = EPI == Epi::SiluMul ? 2 : 1;  // B tiles per output tile (gate, up)
+  __shared__ f32x4 red[SK][NB][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int K = a.K;
+  const int KS = K / 32;
+  const int per = (KS + SK - 1) / SK;
+  const int ks0 = min(KS, wave * per);
+  const int ks1 = min(KS, ks0 + per);
+  const int m0 = blockIdx.y * 16;
+  const int mrow = m0 + (lane & 15);
+  const bool xvalid = mrow < a.M;
+  const char* xp = static_cast<const char*>(a.x) +
+                   (static_cast<int64_t>(min(mrow, a.M - 1)) * K + (lane >> 4) * 8) * 2;
+  const int T = (a.Nout + 15) / 16;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  Top2 best[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) best[q] = top2_empty();
+
+  for (int t = blockIdx.x; t < T; t += gridDim.x) {
+    const int n0 = t * 16;
+    const int nrow = min(n0 + (lane & 15), a.Nout - 1);
+    const bf16_t* wp[NB];
+    if constexpr (EPI == Epi::SiluMul) {
+      wp[0] = static_cast<const bf16_t*>(a.w_a) + static_cast<int64_t>(nrow) * K + (lane >> 4) * 8;
+      wp[NB - 1] = static_cast<const bf16_t*>(a.w_b) + static_cast<int64_t>(nrow) * K + (lane >> 4) * 8;
+    } else {
+      const bf16_t* base;
+      int rr;
+      if (nrow < a.n_a) {
+        base = static_cast<const bf16_t*>(a.w_a);
+        rr = nrow;
+      } else if (nrow < a.n_a + a.n_b) {
+        base = static_cast<const bf16_t*>(a.w_b);
+        rr = nrow - a.n_a;
+      } else {
+        base = static_cast<const bf16_t*>(a.w_c);
+        rr = nrow - a.n_a - a.n_b;
+      }
+      wp[0] = base + static_cast<int64_t>(rr) * K + (lane >> 4) * 8;
+    }
+    f32x4 acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = ks0; s < ks1; s += U) {
+      u32x4 av[U], bv[U][NB];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool ok = s + u < ks1;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) bv[u][b] = ok ? load16_stream(wp[b] + (s + u) * 32) : zero;
+        av[u] = (ok && xvalid) ? load16(xp + (s + u) * 64) : zero;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u]),
+                                                           __builtin_bit_cast(bf16x8, bv[u][b]), acc[b], 0, 0, 0);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) red[wave][b][lane] = acc[b];
+    __syncthreads();
+    if (wave == 0) {
+      f32x4 sum[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        sum[b] = red[0][b][lane];
+#pragma unroll
+        for (int w = 1; w < SK; ++w) sum[b] += red[w][b][lane];
+      }
+      const int n = n0 + (lane & 15);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = m0 + 4 * (lane >> 4) + q;
+        if (m >= a.M || n >= a.Nout) continue;
+        const float v = sum[0][q];
+        if constexpr (EPI == Epi::Store) {
+          a.y[static_cast<int64_t>(m) * a.ldy + n] = v;
+        } else if constexpr (EPI == Epi::AddTo) {
+          a.y[static_cast<int64_t>(m) * a.ldy + n] += v;
+        } else if constexpr (EPI == Epi::SiluMul) {
+          const float s = v / (1.f + expf(-v));
+          static_cast<bf16_t*>(a.y_op)[static_cast<int64_t>(m) * a.ldy + n] = f32_to_bf16(s * sum[NB - 1][q]);
+        } else {
+          if (a.logits) a.logits[static_cast<int64_t>(m) * a.Nout + n] = v;
+          top2_push(best[q], v, n);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if constexpr (EPI == Epi::Argmax) {
+    if (wave == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) {
+          Top2 o;
+          o.v1 = __shfl_xor(best[q].v1, off, 64);
+          o.i1 = __shfl_xor(best[q].i1, off, 64);
+          o.v2 = __shfl_xor(best[q].v2, off, 64);
+          o.pad = 0;
+          best[q] = top2_merge(best[q], o);
+        }
+        const int m = m0 + 4 * (lane >> 4) + q;
+        if ((lane & 15) == 0 && m < a.M) a.partials[static_cast<int64_t>(m) * gridDim.x + blockIdx.x] = best[q];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dispatch
+// Smallest activation-row tile that covers M (one pass over the weights),
+// 16-row slices beyond that.
+int gemv_m_tile(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
+
+bool use_mfma(int M, int K, DType dt) { return dt == DType::BF16 && M > 8 && K % 32 == 0; }
+
+int skinny_sk(int K) { return K >= 4096 ? 8 : 4; }
+
+template <typename TW, int MT, int R, Epi EPI>
+hipError_t launch_lds(GemvArgs& a, dim3 grid, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(MT) * a.K * sizeof(TW);
+  static bool raised = false;
+  if (lds > 64 * 1024 && !raised) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_lds_kernel<TW, MT, R, EPI>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+      return hipErrorInvalidValue;
+    raised = true;
+  }
+  hipLaunchKernelGGL((gemv_lds_kernel<TW, MT, R, EPI>), grid, dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
 template <typename TW, Epi EPI>
 hipError_t launch_typed(GemvArgs& a, int num_cus, hipStream_t s) {
-  const int m_tile = a.M >= 16 ? 16 : a.M >= 8 ? 8 : a.M >= 4 ? 4 : a.M >= 2 ? 2 : 1;
-  // rows per wave: R * MT <= 64
-  const int R = m_tile >= 16 ? 4 : m_tile >= 8 ? 8 : 16;
+  if (use_mfma(a.M, a.K, sizeof(TW) == 2 ? DType::BF16 : DType::F32)) {
+    if constexpr (sizeof(TW) == 2) {
+      const int T = (a.Nout + 15) / 16;
+      int gx = T < num_cus * 4 ? T : num_cus * 4;
+      a.grid_x = gx;
+      dim3 grid(gx, (a.M + 15) / 16);
+      if (skinny_sk(a.K) == 8)
+        hipLaunchKernelGGL((mfma_skinny_kernel<8, 8, EPI>), grid, dim3(512), 0, s, a);
+      else
+        hipLaunchKernelGGL((mfma_skinny_kernel<4, 8, EPI>), grid, dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  const int m_tile = gemv_m_tile(a.M);
+  const int R = m_tile >= 16 ? 4 : m_tile >= 8 ? 8 : 16;  // R * MT <= 64
   const int rg = EPI == Epi::SiluMul ? R / 2 : R;
   const int groups = (a.Nout + rg - 1) / rg;
   int gx = (groups + 3) / 4;
-  const int cap = num_cus * 2;
-  if (gx > cap) gx = cap;
+  if (gx > num_cus) gx = num_cus;
   if (gx < 1) gx = 1;
   a.grid_x = gx;
   dim3 grid(gx, (a.M + m_tile - 1) / m_tile);
   switch (m_tile) {
-    case 16: hipLaunchKernelGGL((gemv_kernel<TW, 16, 4, EPI>), grid, dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((gemv_kernel<TW, 8, 8, EPI>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((gemv_kernel<TW, 4, 16, EPI>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((gemv_kernel<TW, 2, 16, EPI>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((gemv_kernel<TW, 1, 16, EPI>), grid, dim3(256), 0, s, a); break;
+    case 16: return launch_lds<TW, 16, 4, EPI>(a, grid, s);
+    case 8: return launch_lds<TW, 8, 8, EPI>(a, grid, s);
+    case 4: return launch_lds<TW, 4, 16, EPI>(a, grid, s);
+    case 2: return launch_lds<TW, 2, 16, EPI>(a, grid, s);
+    default: return launch_lds<TW, 1, 16, EPI>(a, grid, s);
   }
-  return hipGetLastError();
 }
 
 template <typename TW>
@@ -156,13 +328,22 @@ hipError_t launch_dtype(GemvArgs& a, Epi epi, int num_cus, hipStream_t s) {
 
 }  // namespace
 
-int gemv_grid_x(int M, int Nout, Epi epi, DType, int num_cus) {
-  const int m_tile = M >= 16 ? 16 : M >= 8 ? 8 : M >= 4 ? 4 : M >= 2 ? 2 : 1;
+int gemv_grid_x(int M, int Nout, Epi epi, DType dt, int num_cus, int K) {
+  if (use_mfma(M, K, dt)) {
+    const int T = (Nout + 15) / 16;
+    return T < num_cus * 4 ? T : num_cus * 4;
+  }
+  const int m_tile = gemv_m_tile(M);
   const int R = m_tile >= 16 ? 4 : m_tile >= 8 ? 8 : 16;
   const int rg = epi == Epi::SiluMul ? R / 2 : R;
   int gx = ((Nout + rg - 1) / rg + 3) / 4;
-  if (gx > num_cus * 2) gx = num_cus * 2;
+  if (gx > num_cus) gx = num_cus;
   return gx < 1 ? 1 : gx;
+}
+
+size_t gemv_lds_bytes(int M, int K, DType dt) {
+  if (use_mfma(M, K, dt)) return 0;
+  return static_cast<size_t>(gemv_m_tile(M)) * K * elem_bytes(dt);
 }
 
 hipError_t launch_gemv(GemvArgs& a, Epi epi, DType dt, int num_cus, hipStream_t s) {

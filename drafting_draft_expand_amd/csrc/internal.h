@@ -54,7 +54,8 @@ struct GemvArgs {
   int grid_x;             // filled by the launcher
 };
 hipError_t launch_gemv(GemvArgs& a, Epi epi, DType dt, int num_cus, hipStream_t s);
-int gemv_grid_x(int M, int Nout, Epi epi, DType dt, int num_cus);
+int gemv_grid_x(int M, int Nout, Epi epi, DType dt, int num_cus, int K);
+size_t gemv_lds_bytes(int M, int K, DType dt);  // dynamic LDS of the chosen kernel
 
 // ---------------------------------------------------------------- small kernels
 hipError_t launch_build_fc_input(DType dt, int N, int H, const int32_t* ids, const void* embed,

@@ -22,24 +22,33 @@ __global__ __launch_bounds__(256) void fc_input_kernel(int H_bytes, const int32_
 }
 
 // out[i] = x[row] / sqrt(mean(x[row]^2) + eps) * gain, rounded to the operand
-// dtype; one wave per row, row = row_idx ? row_idx[i] : i.
+// dtype; one workgroup per row, row = row_idx ? row_idx[i] : i.
 template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(int rows, int H, const int32_t* row_idx, const float* x,
-                                                      const T* gain, float eps, T* out) {
-  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (i >= rows) return;
+__global__ __launch_bounds__(256) void rmsnorm_kernel(int H, const int32_t* __restrict__ row_idx,
+                                                      const float* __restrict__ x, const T* __restrict__ gain,
+                                                      float eps, T* __restrict__ out) {
+  __shared__ float part[4];
+  const int i = blockIdx.x;
   const int r = row_idx ? row_idx[i] : i;
-  const float* xr = x + static_cast<int64_t>(r) * H;
+  const f32x4* xr = reinterpret_cast<const f32x4*>(x + static_cast<int64_t>(r) * H);
+  const int nv = H / 4;
   float ss = 0.f;
-  for (int k = lane * 4; k < H; k += 256) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(xr + k);
-    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  for (int v = threadIdx.x; v < nv; v += 256) {
+    const f32x4 q = xr[v];
+    ss += q[0] * q[0] + q[1] * q[1] + q[2] * q[2] + q[3] * q[3];
   }
   ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  ss = part[0] + part[1] + part[2] + part[3];
   const float scale = 1.f / sqrtf(ss / static_cast<float>(H) + eps);
   T* o = out + static_cast<int64_t>(i) * H;
-  for (int k = lane; k < H; k += 64) o[k] = Elem<T>::from_f32(xr[k] * scale * Elem<T>::to_f32(gain[k]));
+  for (int v = threadIdx.x; v < nv; v += 256) {
+    const f32x4 q = xr[v];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[4 * v + e] = Elem<T>::from_f32(q[e] * scale * Elem<T>::to_f32(gain[4 * v + e]));
+  }
 }
 
 // Rotate-half RoPE of q and k at the row's position, q stored as the attention
@@ -137,12 +146,12 @@ hipError_t launch_build_fc_input(DType dt, int N, int H, const int32_t* ids, con
 
 hipError_t launch_rmsnorm(DType dt, int rows, int H, const int32_t* row_idx, const float* x, const void* gain,
                           float eps, void* out, hipStream_t s) {
-  dim3 grid((rows + 3) / 4);
+  dim3 grid(rows);
   if (dt == DType::F32)
-    hipLaunchKernelGGL(rmsnorm_kernel<float>, grid, dim3(256), 0, s, rows, H, row_idx, x,
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, grid, dim3(256), 0, s, H, row_idx, x,
                        static_cast<const float*>(gain), eps, static_cast<float*>(out));
   else
-    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, grid, dim3(256), 0, s, rows, H, row_idx, x,
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, grid, dim3(256), 0, s, H, row_idx, x,
                        static_cast<const bf16_t*>(gain), eps, static_cast<bf16_t*>(out));
   return hipGetLastError();
 }
