@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstring>
 #include <new>
 #include <utility>
@@ -28,6 +29,7 @@ struct pe_model {
   pe_weights w;
   std::vector<pe_layer_weights> layers;
   int num_cus = 0;  // queried on first launch
+  pe::RopeFreq freq; // theta^(-2j/d) in double precision
   Timing timing[3];
 };
 
@@ -43,15 +45,15 @@ inline DType dt(const pe_model* m) { return m->d.dtype == PE_F32 ? DType::F32 : 
 // chip at low concurrency without multiplying the partial-result traffic.
 int attention_splits(int c, int n_kv) {
   const int base = c * n_kv;
-  int s = (128 + base - 1) / base;
+  int s = (1024 + base - 1) / base;
   if (s < 1) s = 1;
-  if (s > 32) s = 32;
+  if (s > 16) s = 16;
   return s;
 }
 
 // Workspace carve-up for one forward call.
 struct Workspace {
-  size_t x, act, qkv, q, attn_part, mlp, top2, f, total;
+  size_t x, act, qkv, q, attn_part, mlp, top2, f, ss0, total;
   int splits, lm_parts;
 };
 
@@ -75,6 +77,7 @@ Workspace plan_workspace(const pe_model* m, int c, int K, int N) {
   w.mlp = off;       off += align_up(size_t(N) * d.inter * eb);
   w.top2 = off;      off += align_up(size_t(S) * w.lm_parts * sizeof(pe::Top2));
   w.f = off;         off += align_up(size_t(S) * H * eb);
+  w.ss0 = off;       off += align_up(size_t((H + 15) / 16) * N * 4);
   w.total = off;
   return w;
 }
@@ -93,6 +96,28 @@ pe_status check_desc(const pe_model_desc* d) {
   if (d->mask_token_id < 0 || d->mask_token_id >= d->vocab) return PE_EINVAL;
   if (!(d->rms_eps > 0.f) || !(d->rope_theta > 0.f)) return PE_EINVAL;
   return PE_OK;
+}
+
+// Fused plan: every projection runs on the MFMA kernel, which gathers the fc
+// input on the fly, applies RoPE + the KV write in the q/k/v epilogue and
+// emits the row sums of squares the LM head needs for the final RMSNorm.
+// Otherwise separate gather / RoPE / final-norm kernels are used.
+bool fused_plan(const pe_model_desc& d, int N) {
+  const pe::DType t = d.dtype == PE_F32 ? pe::DType::F32 : pe::DType::BF16;
+  const int qd = d.n_q * d.head_dim;
+  const int ks[] = {2 * d.hidden, d.hidden, qd, d.inter};
+  for (int k : ks)
+    if (!pe::gemv_uses_mfma(N, k, t)) return false;
+  return d.hidden % 32 == 0 && d.head_dim % 16 == 0;
+}
+
+// The final RMSNorm rides in the LM head when the down projection emits row
+// sums of squares (weight-streaming MFMA kernel) and the LM head stages its
+// rows itself (LDS GEMV or weight-streaming MFMA).
+bool fused_final_norm(const pe_model_desc& d, int N, int S) {
+  const pe::DType t = d.dtype == PE_F32 ? pe::DType::F32 : pe::DType::BF16;
+  return pe::proj_kernel(N, d.inter, t) == pe::ProjKernel::Skinny &&
+         pe::proj_kernel(S, d.hidden, t) != pe::ProjKernel::Tiled;
 }
 
 int num_cus(pe_model* m) {
@@ -171,6 +196,10 @@ pe_status pe_model_create(const pe_model_desc* desc, const pe_weights* w, pe_mod
   m->d = *desc;
   m->w = *w;
   if (desc->n_layers > 0) m->layers.assign(w->layers, w->layers + desc->n_layers);
+  for (int j = 0; j < 64; ++j)
+    m->freq.inv[j] = desc->n_layers > 0 && j < desc->head_dim / 2
+                         ? std::pow(static_cast<double>(desc->rope_theta), -2.0 * j / desc->head_dim)
+                         : 0.0;
   m->w.layers = m->layers.empty() ? nullptr : m->layers.data();
   *out = m;
   return PE_OK;
@@ -263,78 +292,148 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
   void* mlp = wb + ws.mlp;
   pe::Top2* top2 = reinterpret_cast<pe::Top2*>(wb + ws.top2);
   void* f = wb + ws.f;
+  float* ss0 = reinterpret_cast<float*>(wb + ws.ss0);
   const int cus = num_cus(m);
 
-  // fc over [emb(id) ; h]
-  PE_HIP(pe::launch_build_fc_input(t, N, H, draft_ids, m->w.embed, draft_hidden, act, stream));
+  const int ss_tiles = (H + 15) / 16;
+  const bool fused = fused_plan(d, N);
+  const bool fnorm = fused && fused_final_norm(d, N, S);
+  // attention and LM head are shared by both plans
+  auto attention = [&](int l) -> pe_status {
+    pe::AttnArgs at{};
+    at.c = c; at.N = N; at.n_q = d.n_q; at.n_kv = d.n_kv; at.d = d.head_dim;
+    at.block_size = d.block_size; at.max_blocks = max_blocks; at.splits = ws.splits; at.dtype = t;
+    at.q = qrot; at.pos = draft_pos; at.rejected = is_rejected; at.cu_draft = cu_draft;
+    at.kv_lens = kv_lens; at.block_table = block_table; at.k_cache = k_cache[l];
+    at.v_cache = v_cache[l]; at.partial = part; at.out = act;
+    TimedScope ts(m, PE_KERNEL_ATTENTION, stream);
+    PE_HIP(pe::launch_attention(at, stream));
+    return PE_OK;
+  };
+  auto proj = [&](pe::GemvArgs& g, pe::Epi e) -> pe_status {
+    PE_HIP(pe::launch_gemv(g, e, t, cus, stream));
+    return PE_OK;
+  };
+  pe_status st;
+
+  if (fused) {
+    // fc over [emb(id) ; h] gathered on the fly; epilogue emits row sums of squares
+    {
+      pe::GemvArgs g{};
+      g.M = N; g.Nout = H; g.K = 2 * H; g.amode = pe::AMode::Gather;
+      g.ids = draft_ids; g.embed = m->w.embed; g.x2 = draft_hidden;
+      g.w_a = g.w_b = g.w_c = m->w.w_fc; g.n_a = H; g.n_b = 0;
+      g.y = x; g.ldy = H;
+      if ((st = proj(g, pe::Epi::Store)) != PE_OK) return st;
+    }
+    for (int l = 0; l < d.n_layers; ++l) {
+      const pe_layer_weights& L = m->layers[l];
+      // RMSNorm as its own pass: forming it inside the projection would make
+      // every workgroup re-read the fp32 rows (twice the operand traffic)
+      PE_HIP(pe::launch_rmsnorm(t, N, H, nullptr, x, L.ln1, d.rms_eps, act, stream));
+      {
+        // q/k/v -> RoPE -> q operand + paged KV write
+        pe::GemvArgs g{};
+        g.M = N; g.Nout = qd + 2 * kvd; g.K = H; g.amode = pe::AMode::Plain; g.x = act;
+        g.w_a = L.wq; g.n_a = qd; g.w_b = L.wk; g.n_b = kvd; g.w_c = L.wv;
+        g.rope.n_q = d.n_q; g.rope.n_kv = d.n_kv; g.rope.d = d.head_dim; g.rope.block_size = d.block_size;
+        g.rope.freq = m->freq; g.rope.pos = draft_pos; g.rope.slot = slot_mapping;
+        g.rope.rejected = is_rejected; g.rope.q_out = qrot; g.rope.k_cache = k_cache[l];
+        g.rope.v_cache = v_cache[l];
+        if ((st = proj(g, pe::Epi::QkvRope)) != PE_OK) return st;
+      }
+      if ((st = attention(l)) != PE_OK) return st;
+      {
+        pe::GemvArgs g{};
+        g.M = N; g.Nout = H; g.K = qd; g.amode = pe::AMode::Plain; g.x = act;
+        g.w_a = g.w_b = g.w_c = L.wo; g.n_a = H; g.n_b = 0;
+        g.y = x; g.ldy = H;
+        if ((st = proj(g, pe::Epi::AddTo)) != PE_OK) return st;
+      }
+      PE_HIP(pe::launch_rmsnorm(t, N, H, nullptr, x, L.ln2, d.rms_eps, act, stream));
+      {
+        pe::GemvArgs g{};
+        g.M = N; g.Nout = d.inter; g.K = H; g.amode = pe::AMode::Plain; g.x = act;
+        g.w_a = L.w_gate; g.w_b = L.w_up; g.w_c = L.w_up; g.n_a = d.inter; g.n_b = d.inter;
+        g.y_op = mlp; g.ldy = d.inter;
+        if ((st = proj(g, pe::Epi::SiluMul)) != PE_OK) return st;
+      }
+      {
+        pe::GemvArgs g{};
+        g.M = N; g.Nout = H; g.K = d.inter; g.amode = pe::AMode::Plain; g.x = mlp;
+        g.w_a = g.w_b = g.w_c = L.w_down; g.n_a = H; g.n_b = 0;
+        g.y = x; g.ldy = H; g.ss_out = fnorm && l == d.n_layers - 1 ? ss0 : nullptr;
+        if ((st = proj(g, pe::Epi::AddTo)) != PE_OK) return st;
+      }
+    }
+  } else {
+    PE_HIP(pe::launch_build_fc_input(t, N, H, draft_ids, m->w.embed, draft_hidden, act, stream));
+    {
+      pe::GemvArgs g{};
+      g.M = N; g.Nout = H; g.K = 2 * H; g.amode = pe::AMode::Plain; g.x = act;
+      g.w_a = m->w.w_fc; g.n_a = H; g.w_b = g.w_c = m->w.w_fc; g.n_b = 0;
+      g.y = x; g.ldy = H;
+      if ((st = proj(g, pe::Epi::Store)) != PE_OK) return st;
+    }
+    for (int l = 0; l < d.n_layers; ++l) {
+      const pe_layer_weights& L = m->layers[l];
+      PE_HIP(pe::launch_rmsnorm(t, N, H, nullptr, x, L.ln1, d.rms_eps, act, stream));
+      {
+        pe::GemvArgs g{};
+        g.M = N; g.Nout = qd + 2 * kvd; g.K = H; g.amode = pe::AMode::Plain; g.x = act;
+        g.w_a = L.wq; g.n_a = qd; g.w_b = L.wk; g.n_b = kvd; g.w_c = L.wv;
+        g.y = qkv; g.ldy = qd + 2 * kvd;
+        if ((st = proj(g, pe::Epi::Store)) != PE_OK) return st;
+      }
+      {
+        pe::RopeArgs r{};
+        r.N = N; r.n_q = d.n_q; r.n_kv = d.n_kv; r.d = d.head_dim; r.block_size = d.block_size;
+        r.freq = m->freq; r.dtype = t; r.qkv = qkv; r.pos = draft_pos; r.slot = slot_mapping;
+        r.rejected = is_rejected; r.q_out = qrot; r.k_cache = k_cache[l]; r.v_cache = v_cache[l];
+        PE_HIP(pe::launch_rope_kvwrite(r, stream));
+      }
+      if ((st = attention(l)) != PE_OK) return st;
+      {
+        pe::GemvArgs g{};
+        g.M = N; g.Nout = H; g.K = qd; g.amode = pe::AMode::Plain; g.x = act;
+        g.w_a = g.w_b = g.w_c = L.wo; g.n_a = H; g.n_b = 0;
+        g.y = x; g.ldy = H;
+        if ((st = proj(g, pe::Epi::AddTo)) != PE_OK) return st;
+      }
+      PE_HIP(pe::launch_rmsnorm(t, N, H, nullptr, x, L.ln2, d.rms_eps, act, stream));
+      {
+        pe::GemvArgs g{};
+        g.M = N; g.Nout = d.inter; g.K = H; g.amode = pe::AMode::Plain; g.x = act;
+        g.w_a = L.w_gate; g.w_b = L.w_up; g.w_c = L.w_up; g.n_a = d.inter; g.n_b = d.inter;
+        g.y_op = mlp; g.ldy = d.inter;
+        if ((st = proj(g, pe::Epi::SiluMul)) != PE_OK) return st;
+      }
+      {
+        pe::GemvArgs g{};
+        g.M = N; g.Nout = H; g.K = d.inter; g.amode = pe::AMode::Plain; g.x = mlp;
+        g.w_a = g.w_b = g.w_c = L.w_down; g.n_a = H; g.n_b = 0;
+        g.y = x; g.ldy = H;
+        if ((st = proj(g, pe::Epi::AddTo)) != PE_OK) return st;
+      }
+    }
+  }
+  if (!fnorm) PE_HIP(pe::launch_rmsnorm(t, S, H, sample_idx, x, m->w.ln_f, d.rms_eps, f, stream));
+  // LM head + argmax over the sampled rows
   {
     pe::GemvArgs g{};
-    g.M = N; g.Nout = H; g.K = 2 * H; g.x = act;
-    g.w_a = m->w.w_fc; g.n_a = H; g.w_b = g.w_c = m->w.w_fc; g.n_b = 0;
-    g.y = x; g.ldy = H;
-    PE_HIP(pe::launch_gemv(g, pe::Epi::Store, t, cus, stream));
-  }
-  for (int l = 0; l < d.n_layers; ++l) {
-    const pe_layer_weights& L = m->layers[l];
-    PE_HIP(pe::launch_rmsnorm(t, N, H, nullptr, x, L.ln1, d.rms_eps, act, stream));
-    {
-      pe::GemvArgs g{};
-      g.M = N; g.Nout = qd + 2 * kvd; g.K = H; g.x = act;
-      g.w_a = L.wq; g.n_a = qd; g.w_b = L.wk; g.n_b = kvd; g.w_c = L.wv;
-      g.y = qkv; g.ldy = qd + 2 * kvd;
-      PE_HIP(pe::launch_gemv(g, pe::Epi::Store, t, cus, stream));
+    g.M = S; g.Nout = d.vocab; g.K = H;
+    if (fnorm) {
+      g.amode = pe::AMode::Norm; g.xf = x; g.rows = sample_idx; g.gain = m->w.ln_f; g.ss = ss0;
+      g.ss_tiles = ss_tiles; g.ss_ld = N; g.eps = d.rms_eps;
+    } else {
+      g.amode = pe::AMode::Plain; g.x = f;
     }
-    {
-      pe::RopeArgs r{};
-      r.N = N; r.n_q = d.n_q; r.n_kv = d.n_kv; r.d = d.head_dim; r.block_size = d.block_size;
-      r.theta = d.rope_theta; r.dtype = t; r.qkv = qkv; r.pos = draft_pos; r.slot = slot_mapping;
-      r.rejected = is_rejected; r.q_out = qrot; r.k_cache = k_cache[l]; r.v_cache = v_cache[l];
-      PE_HIP(pe::launch_rope_kvwrite(r, stream));
-    }
-    {
-      pe::AttnArgs at{};
-      at.c = c; at.N = N; at.n_q = d.n_q; at.n_kv = d.n_kv; at.d = d.head_dim;
-      at.block_size = d.block_size; at.max_blocks = max_blocks; at.splits = ws.splits; at.dtype = t;
-      at.q = qrot; at.pos = draft_pos; at.rejected = is_rejected; at.cu_draft = cu_draft;
-      at.kv_lens = kv_lens; at.block_table = block_table; at.k_cache = k_cache[l];
-      at.v_cache = v_cache[l]; at.partial = part; at.out = act;
-      TimedScope ts(m, PE_KERNEL_ATTENTION, stream);
-      PE_HIP(pe::launch_attention(at, stream));
-    }
-    {
-      pe::GemvArgs g{};
-      g.M = N; g.Nout = H; g.K = qd; g.x = act;
-      g.w_a = g.w_b = g.w_c = L.wo; g.n_a = H; g.n_b = 0;
-      g.y = x; g.ldy = H;
-      PE_HIP(pe::launch_gemv(g, pe::Epi::AddTo, t, cus, stream));
-    }
-    PE_HIP(pe::launch_rmsnorm(t, N, H, nullptr, x, L.ln2, d.rms_eps, act, stream));
-    {
-      pe::GemvArgs g{};
-      g.M = N; g.Nout = d.inter; g.K = H; g.x = act;
-      g.w_a = L.w_gate; g.w_b = L.w_up; g.w_c = L.w_up; g.n_a = d.inter; g.n_b = d.inter;
-      g.y_op = mlp; g.ldy = d.inter;
-      PE_HIP(pe::launch_gemv(g, pe::Epi::SiluMul, t, cus, stream));
-    }
-    {
-      pe::GemvArgs g{};
-      g.M = N; g.Nout = H; g.K = d.inter; g.x = mlp;
-      g.w_a = g.w_b = g.w_c = L.w_down; g.n_a = H; g.n_b = 0;
-      g.y = x; g.ldy = H;
-      PE_HIP(pe::launch_gemv(g, pe::Epi::AddTo, t, cus, stream));
-    }
-  }
-  // final norm on the sampled rows, LM head + argmax
-  PE_HIP(pe::launch_rmsnorm(t, S, H, sample_idx, x, m->w.ln_f, d.rms_eps, f, stream));
-  {
-    pe::GemvArgs g{};
-    g.M = S; g.Nout = d.vocab; g.K = H; g.x = f;
     g.w_a = g.w_b = g.w_c = m->w.w_lm; g.n_a = d.vocab; g.n_b = 0;
     g.logits = logits; g.partials = top2;
     if (pe::gemv_grid_x(S, d.vocab, pe::Epi::Argmax, t, cus, H) > ws.lm_parts) return PE_EUNSUPPORTED;
     {
       TimedScope ts(m, PE_KERNEL_LM_HEAD, stream);
-      PE_HIP(pe::launch_gemv(g, pe::Epi::Argmax, t, cus, stream));
+      if ((st = proj(g, pe::Epi::Argmax)) != PE_OK) return st;
     }
     PE_HIP(pe::launch_argmax_finalize(S, g.grid_x, top2, draft_tokens, top2_gap, stream));
   }

@@ -144,23 +144,25 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
 // bf16, head_dim 64/128: the same split-KV attention on MFMA.
 //
 // A workgroup of 8 waves owns up to 128 queries (16 per wave) of one
-// (sequence, kv head, split).  Per 32-key tile the waves share K (row-major)
+// (sequence, kv head, split).  Per 64-key tile the waves share K (row-major)
 // and V (transposed) in LDS.  Scores are formed transposed, S^T = K Q^T with
 // v_mfma_f32_16x16x32_bf16 (keys are the A rows, the wave's queries the B
 // columns), so each lane owns one query column: the online-softmax row
 // statistics need only the 4 lanes that share that column, and the
-// probabilities are already in the B-operand layout of O^T += V^T P^T.  The
-// MFMA's 32 k-slots of that product enumerate keys 4j..4j+3 and 16+4j..16+4j+3
-// for lane group j, the order in which the score tiles hold them.  The next
-// tile's K/V pieces are fetched into registers while the current one is used.
+// probabilities are already in the B-operand layout of O^T += V^T P^T.  In
+// that product the MFMA's 32 k-slots of each 32-key half enumerate keys
+// 4j..4j+3 and 16+4j..16+4j+3 for lane group j, the order in which the score
+// tiles hold them.  K/V pieces of the next two tiles are kept in flight in
+// registers while the current tile is consumed from LDS.
 template <int D>
 __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
-  constexpr int KT = 32;
+  constexpr int KT = 64;
   constexpr int KP = D + 8;    // padded K row (elements)
   constexpr int VP = KT + 8;   // padded V^T row (elements)
   constexpr int DT = D / 16;   // O^T tiles
   constexpr int KK = D / 32;   // k-steps of S^T
-  constexpr int PER = KT * D / 8 / 512 > 0 ? KT * D / 8 / 512 : 1;  // 16-byte pieces per thread
+  constexpr int PER = KT * D / 8 / 512;  // 16-byte K (and V) pieces per thread per tile
+  static_assert(PER >= 1, "tile too small for the workgroup");
   __shared__ bf16_t ks[KT * KP];
   __shared__ bf16_t vt[D * VP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, j = lane >> 4;
@@ -171,6 +173,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   const int chunk = ((kvlen + a.splits - 1) / a.splits + KT - 1) / KT * KT;
   const int kb = sp * chunk;
   const int ke = min(kvlen, kb + chunk);
+  const int ntiles = ke > kb ? (ke - kb + KT - 1) / KT : 0;
   const int nqry = (r1 - r0) * grp;
   const float sl2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));  // scale * log2(e)
   const bf16_t* qin = static_cast<const bf16_t*>(a.q);
@@ -178,7 +181,38 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   const bf16_t* vc = static_cast<const bf16_t*>(a.v_cache);
   const int32_t* bt = a.block_table + static_cast<int64_t>(i) * a.max_blocks;
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  const bool loader = tid < KT * D / 8;
+
+  u32x4 kr[2][PER], vr[2][PER];
+  auto fetch = [&](int t, int set) {
+#pragma unroll
+    for (int pp = 0; pp < PER; ++pp) {
+      const int piece = tid + 512 * pp;
+      const int key = piece / (D / 8), c8 = piece % (D / 8);
+      const int p = kb + t * KT + key;
+      kr[set][pp] = zero;
+      vr[set][pp] = zero;
+      if (p < ke) {
+        const int64_t blk = bt[p / a.block_size];
+        const int64_t off = ((blk * a.n_kv + g) * a.block_size + p % a.block_size) * D + c8 * 8;
+        kr[set][pp] = load16(kc + off);
+        vr[set][pp] = load16(vc + off);
+      }
+    }
+  };
+  auto stash = [&](int set) {
+#pragma unroll
+    for (int pp = 0; pp < PER; ++pp) {
+      const int piece = tid + 512 * pp;
+      const int key = piece / (D / 8), c8 = piece % (D / 8);
+      store16(ks + key * KP + c8 * 8, kr[set][pp]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = vr[set][pp][e];
+        vt[(c8 * 8 + 2 * e) * VP + key] = static_cast<bf16_t>(w & 0xffffu);
+        vt[(c8 * 8 + 2 * e + 1) * VP + key] = static_cast<bf16_t>(w >> 16);
+      }
+    }
+  };
 
   for (int qb = 0; qb < nqry; qb += 128) {
     const int qn = qb + wave * 16 + (lane & 15);
@@ -195,42 +229,18 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int t = 0; t < DT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // register prefetch of one K/V tile: thread -> (key, 8-element column piece)
-    auto fetch = [&](int kt0, u32x4& kv, u32x4& vv) {
-      kv = zero;
-      vv = zero;
-      if (!loader) return;
-      const int key = tid / (D / 8), c8 = tid % (D / 8);
-      const int p = kt0 + key;
-      if (p < ke) {
-        const int64_t blk = bt[p / a.block_size];
-        const int64_t off = ((blk * a.n_kv + g) * a.block_size + p % a.block_size) * D + c8 * 8;
-        kv = load16(kc + off);
-        vv = load16(vc + off);
-      }
-    };
-    u32x4 kn, vn;
-    static_assert(PER == 1, "one 16-byte K and V piece per loader thread");
-    fetch(kb, kn, vn);
-    for (int kt0 = kb; kt0 < ke; kt0 += KT) {
+    if (ntiles > 0) fetch(0, 0);
+    if (ntiles > 1) fetch(1, 1);
+    for (int t = 0; t < ntiles; ++t) {
+      const int kt0 = kb + t * KT;
       __syncthreads();
-      if (loader) {
-        const int key = tid / (D / 8), c8 = tid % (D / 8);
-        store16(ks + key * KP + c8 * 8, kn);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t w = vn[e];
-          vt[(c8 * 8 + 2 * e) * VP + key] = static_cast<bf16_t>(w & 0xffffu);
-          vt[(c8 * 8 + 2 * e + 1) * VP + key] = static_cast<bf16_t>(w >> 16);
-        }
-      }
+      stash(t & 1);
       __syncthreads();
-      if (kt0 + KT < ke) fetch(kt0 + KT, kn, vn);
+      if (t + 2 < ntiles) fetch(t + 2, t & 1);
 
-      // S^T for keys [0,16) and [16,32) of the tile
-      f32x4 st[2];
+      f32x4 st[4];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < 4; ++mt) {
         st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
@@ -239,25 +249,25 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
                                                            __builtin_bit_cast(bf16x8, qf[kk]), st[mt], 0, 0, 0);
         }
       }
-      float sv[8];
+      float sv[16];
       float mx = -INFINITY;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int p = kt0 + mt * 16 + 4 * j + q;
-          const float s = (p < ke && p <= qpos) ? st[mt][q] * sl2 : -INFINITY;
-          sv[mt * 4 + q] = s;
-          mx = fmaxf(mx, s);
+          const float sc = (p < ke && p <= qpos) ? st[mt][q] * sl2 : -INFINITY;
+          sv[mt * 4 + q] = sc;
+          mx = fmaxf(mx, sc);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = fmaxf(m_run, mx);
       const float corr = m_run == -INFINITY ? (m_new == -INFINITY ? 1.f : 0.f) : exp2f(m_run - m_new);
       float rs = 0.f;
-      uint32_t pk[4];
+      uint32_t pk[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < 8; ++e) {
         const float p0 = sv[2 * e] == -INFINITY ? 0.f : exp2f(sv[2 * e] - m_new);
         const float p1 = sv[2 * e + 1] == -INFINITY ? 0.f : exp2f(sv[2 * e + 1] - m_new);
         rs += p0 + p1;
@@ -267,19 +277,22 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
       rs += __shfl_xor(rs, 32, 64);
       l_run = l_run * corr + rs;
       m_run = m_new;
-      const u32x4 pb = {pk[0], pk[1], pk[2], pk[3]};
 #pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        o[t] *= corr;
-        const bf16_t* vr = vt + (t * 16 + (lane & 15)) * VP;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr + 4 * j);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16 + 4 * j);
-        const u32x4 af = {lo.x, lo.y, hi.x, hi.y};
-        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af),
-                                                       __builtin_bit_cast(bf16x8, pb), o[t], 0, 0, 0);
+      for (int hf = 0; hf < 2; ++hf) {
+        const u32x4 pb = {pk[4 * hf], pk[4 * hf + 1], pk[4 * hf + 2], pk[4 * hf + 3]};
+#pragma unroll
+        for (int t2 = 0; t2 < DT; ++t2) {
+          if (hf == 0) o[t2] *= corr;
+          const bf16_t* vr_ = vt + (t2 * 16 + (lane & 15)) * VP + hf * 32;
+          const uint2 lo = *reinterpret_cast<const uint2*>(vr_ + 4 * j);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vr_ + 16 + 4 * j);
+          const u32x4 af = {lo.x, lo.y, hi.x, hi.y};
+          o[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af),
+                                                          __builtin_bit_cast(bf16x8, pb), o[t2], 0, 0, 0);
+        }
       }
     }
-    if (qn < nqry) {
+    if (qn < nqry && !a.rejected[row]) {
       float* out = a.partial + ((static_cast<int64_t>(row) * a.n_q + h) * a.splits + sp) * (D + 2);
 #pragma unroll
       for (int t = 0; t < DT; ++t)

@@ -110,6 +110,16 @@ __device__ __forceinline__ float wave_reduce_scatter(float (&v)[NV], int lane) {
 template <int NV> struct Log2 { static constexpr int value = 1 + Log2<NV / 2>::value; };
 template <> struct Log2<1> { static constexpr int value = 0; };
 
+// cos/sin of the rotary angle p * inv_freq: the product and its reduction to
+// [-pi, pi] are done in double precision, the final sincos in fp32, so the
+// angle error stays ~1e-7 rad even at positions of tens of thousands.
+__device__ __forceinline__ void rope_cos_sin(int pos, double inv_freq, float& c, float& s) {
+  const double ang = static_cast<double>(pos) * inv_freq;
+  const double two_pi = 6.283185307179586476925286766559;
+  const double r = ang - two_pi * rint(ang * (1.0 / two_pi));
+  sincosf(static_cast<float>(r), &s, &c);
+}
+
 // Best and runner-up logit of a set of vocabulary rows (ties -> lowest id).
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);

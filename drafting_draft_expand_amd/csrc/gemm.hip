@@ -1,0 +1,328 @@
+// Tiled bf16 MFMA GEMM for many activation rows (M > 16): the drafter's
+// projections at high concurrency and the LM head over c*K sampled rows.
+//
+// C[m, n] = sum_k A[m, k] * W[n, k], A and W both row-major with K contiguous.
+// Four waves in a 2 x 2 grid per workgroup; each wave owns a WM x WN block of
+// v_mfma_f32_16x16x32_bf16 tiles.  Per K step the next A/W tiles are fetched
+// into registers while the current ones are read from LDS (rows padded by 16
+// bytes so the 16-row fragment reads spread over the banks), then written to
+// the other LDS buffer: one barrier per K step.  LDS traffic per MFMA falls as
+// the wave block grows, so the largest tile that still gives every CU work
+// is chosen: 256 x 256 (128 x 128 per wave, 256 accumulator registers) for the
+// LM head, smaller ones for the layer projections.
+//
+// Tile order is XCD-aware: workgroups are dealt round-robin to the 8 XCDs, so
+// the logical tile index is taken from (blockIdx % 8, blockIdx / 8) such that
+// the M tiles sharing one W tile run on the same XCD and reuse it from that
+// XCD's L2 instead of fetching it from HBM once per M tile.
+//
+// Epilogues (same contracts as the weight-streaming kernels): store, residual
+// add, SiLU(gate)*up (each wave's 8 N tiles are 4 gate + 4 matching up tiles),
+// q/k/v with RoPE and the paged KV write (each 16-column MFMA tile holds 8
+// rotary pairs, columns c and c^8), and LM-head argmax candidates per
+// (row, 256-column tile).
+#include "common.h"
+
+namespace pe {
+namespace {
+
+// W row (global) loaded into B-tile row r of N tile nt.
+template <Epi EPI, int BN, int WN>
+__device__ __forceinline__ int b_row(const GemvArgs& a, int nt, int r) {
+  if constexpr (EPI == Epi::SiluMul) {
+    // BN/2 output columns per tile: wave column wn holds WN/2 gate rows then
+    // the WN/2 matching up rows
+    const int wn = r / WN, rr = r % WN;
+    return nt * (BN / 2) + wn * (WN / 2) + (rr % (WN / 2));
+  } else if constexpr (EPI == Epi::QkvRope) {
+    const int col = nt * BN + r;
+    const int per_head = a.rope.d / 16;
+    const int t = col / 16, c = col % 16;
+    const int head = t / per_head, p = t - head * per_head;
+    return head * a.rope.d + 8 * p + (c & 7) + (c >= 8 ? a.rope.d / 2 : 0);
+  } else {
+    return nt * BN + r;
+  }
+}
+
+template <Epi EPI, int BN, int WN>
+__device__ __forceinline__ const bf16_t* b_ptr(const GemvArgs& a, int nt, int r) {
+  const int K = a.K;
+  const int n = min(b_row<EPI, BN, WN>(a, nt, r), a.Nout - 1);
+  if constexpr (EPI == Epi::SiluMul) {
+    return static_cast<const bf16_t*>((r % WN) < WN / 2 ? a.w_a : a.w_b) + static_cast<int64_t>(n) * K;
+  } else {
+    if (n < a.n_a) return static_cast<const bf16_t*>(a.w_a) + static_cast<int64_t>(n) * K;
+    if (n < a.n_a + a.n_b) return static_cast<const bf16_t*>(a.w_b) + static_cast<int64_t>(n - a.n_a) * K;
+    return static_cast<const bf16_t*>(a.w_c) + static_cast<int64_t>(n - a.n_a - a.n_b) * K;
+  }
+}
+
+template <AMode MODE>
+__device__ __forceinline__ u32x4 a_load(const GemvArgs& a, int m, int k) {
+  if constexpr (MODE == AMode::Gather) {
+    const int half = a.K / 2;
+    if (k < half) return load16(static_cast<const bf16_t*>(a.embed) + static_cast<int64_t>(a.ids[m]) * half + k);
+    return load16(static_cast<const bf16_t*>(a.x2) + static_cast<int64_t>(m) * half + (k - half));
+  } else {
+    return load16(static_cast<const bf16_t*>(a.x) + static_cast<int64_t>(m) * a.K + k);
+  }
+}
+
+template <int BM, int BN, int BK, Epi EPI, AMode MODE>
+__global__ __launch_bounds__(256) void gemm_kernel(GemvArgs a, int num_m, int num_n) {
+  constexpr int WM = BM / 2, WN = BN / 2;     // wave block
+  constexpr int TM = WM / 16, TN = WN / 16;   // MFMA tiles per wave
+  constexpr int LDT = BK + 8;                 // padded LDS row, elements
+  constexpr int CPR = BK / 8;                 // 16-byte chunks per tile row
+  constexpr int NA = BM * CPR / 256, NB = BN * CPR / 256;  // chunks per thread
+  static_assert(NA >= 1 && NB >= 1, "tile too small");
+  __shared__ bf16_t As[2][BM * LDT];
+  __shared__ bf16_t Bs[2][BN * LDT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  // XCD-aware tile order: the M tiles of one W tile land on one XCD
+  const int total = num_m * num_n;
+  const int per_xcd = (total + 7) / 8;
+  const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (L >= total) return;
+  const int mt = L % num_m, nt = L / num_m;
+  const int m0 = mt * BM;
+  const int nk = a.K / BK;
+
+  const bf16_t* bp[NB];
+  int a_row[NA], a_col[NA], b_r[NB], b_col[NB];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int c = tid + 256 * i;
+    a_row[i] = c / CPR;
+    a_col[i] = (c % CPR) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int c = tid + 256 * i;
+    b_r[i] = c / CPR;
+    b_col[i] = (c % CPR) * 8;
+    bp[i] = b_ptr<EPI, BN, WN>(a, nt, b_r[i]) + b_col[i];
+  }
+  u32x4 ra[NA], rb[NB];
+  auto fetch = [&](int kt) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) ra[i] = a_load<MODE>(a, min(m0 + a_row[i], a.M - 1), k0 + a_col[i]);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) rb[i] = load16(bp[i] + k0);
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) store16(&As[buf][a_row[i] * LDT + a_col[i]], ra[i]);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) store16(&Bs[buf][b_r[i] * LDT + b_col[i]], rb[i]);
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int jn = 0; jn < TN; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  const int l16 = lane & 15, lq = lane >> 4;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) fetch(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      u32x4 af[TM], bf[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const u32x4*>(&As[cur][(wm * WM + i * 16 + l16) * LDT + ks * 32 + lq * 8]);
+#pragma unroll
+      for (int jn = 0; jn < TN; ++jn)
+        bf[jn] = *reinterpret_cast<const u32x4*>(&Bs[cur][(wn * WN + jn * 16 + l16) * LDT + ks * 32 + lq * 8]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int jn = 0; jn < TN; ++jn)
+          acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[i]),
+                                                               __builtin_bit_cast(bf16x8, bf[jn]), acc[i][jn], 0, 0,
+                                                               0);
+    }
+    if (kt + 1 < nk) stash(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  if constexpr (EPI == Epi::Store || EPI == Epi::AddTo) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int jn = 0; jn < TN; ++jn) {
+        const int n = nt * BN + wn * WN + jn * 16 + l16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = m0 + wm * WM + i * 16 + lq * 4 + q;
+          if (m >= a.M || n >= a.Nout) continue;
+          float* y = a.y + static_cast<int64_t>(m) * a.ldy + n;
+          if constexpr (EPI == Epi::AddTo) *y += acc[i][jn][q];
+          else *y = acc[i][jn][q];
+        }
+      }
+  } else if constexpr (EPI == Epi::SiluMul) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int jn = 0; jn < TN / 2; ++jn) {
+        const int n = nt * (BN / 2) + wn * (WN / 2) + jn * 16 + l16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = m0 + wm * WM + i * 16 + lq * 4 + q;
+          if (m >= a.M || n >= a.Nout) continue;
+          const float gt = acc[i][jn][q];
+          const float sg = gt / (1.f + expf(-gt));
+          static_cast<bf16_t*>(a.y_op)[static_cast<int64_t>(m) * a.ldy + n] =
+              f32_to_bf16(sg * acc[i][jn + TN / 2][q]);
+        }
+      }
+  } else if constexpr (EPI == Epi::QkvRope) {
+    const RopeOut& ro = a.rope;
+    const int d = ro.d;
+#pragma unroll
+    for (int jn = 0; jn < TN; ++jn) {
+      const int col = nt * BN + wn * WN + jn * 16 + l16;
+      const int n = b_row<EPI, BN, WN>(a, nt, wn * WN + jn * 16 + l16);
+      const int head = n / d;
+      const int e = n - head * d;
+      const bool rotate = head < ro.n_q + ro.n_kv;
+      const double inv_freq = ro.freq.inv[e % (d / 2)];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = m0 + wm * WM + i * 16 + lq * 4 + q;
+          const float v = acc[i][jn][q];
+          const float partner = __shfl_xor(v, 8, 64);
+          if (m >= a.M || col >= a.Nout || ro.rejected[m]) continue;
+          float out = v;
+          if (rotate) {
+            float cs, sn;
+            rope_cos_sin(ro.pos[m], inv_freq, cs, sn);
+            out = (l16 & 8) == 0 ? v * cs - partner * sn : v * cs + partner * sn;
+          }
+          if (head < ro.n_q) {
+            static_cast<bf16_t*>(ro.q_out)[(static_cast<int64_t>(m) * ro.n_q + head) * d + e] = f32_to_bf16(out);
+          } else {
+            const int64_t slot = ro.slot[m];
+            if (slot < 0) continue;
+            const bool is_k = head < ro.n_q + ro.n_kv;
+            const int g = is_k ? head - ro.n_q : head - ro.n_q - ro.n_kv;
+            const int64_t blk = slot / ro.block_size;
+            const int off = static_cast<int>(slot - blk * ro.block_size);
+            static_cast<bf16_t*>(is_k ? ro.k_cache : ro.v_cache)[((blk * ro.n_kv + g) * ro.block_size + off) * d + e] =
+                f32_to_bf16(out);
+          }
+        }
+    }
+  } else {  // Argmax over this tile's BN columns, per row
+    Top2* red = reinterpret_cast<Top2*>(&As[0][0]);  // [2 wave columns][BM rows]
+    static_assert(2 * BM * sizeof(Top2) <= sizeof(As) / 2, "argmax scratch must fit one LDS buffer");
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = m0 + wm * WM + i * 16 + lq * 4 + q;
+        Top2 t = top2_empty();
+#pragma unroll
+        for (int jn = 0; jn < TN; ++jn) {
+          const int n = nt * BN + wn * WN + jn * 16 + l16;
+          if (n < a.Nout) {
+            const float v = acc[i][jn][q];
+            if (a.logits && m < a.M) a.logits[static_cast<int64_t>(m) * a.Nout + n] = v;
+            top2_push(t, v, n);
+          }
+        }
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) {
+          Top2 o;
+          o.v1 = __shfl_xor(t.v1, off, 64);
+          o.i1 = __shfl_xor(t.i1, off, 64);
+          o.v2 = __shfl_xor(t.v2, off, 64);
+          o.pad = 0;
+          t = top2_merge(t, o);
+        }
+        if (l16 == 0) red[wn * BM + wm * WM + i * 16 + lq * 4 + q] = t;
+      }
+    __syncthreads();
+    for (int r = tid; r < BM; r += 256) {
+      const int m = m0 + r;
+      if (m < a.M) a.partials[static_cast<int64_t>(m) * num_n + nt] = top2_merge(red[r], red[BM + r]);
+    }
+  }
+}
+
+// Tile shapes: {BM, BN, BK}.
+struct TileCfg {
+  int bm, bn;
+};
+constexpr TileCfg kLarge{256, 256}, kMedium{128, 128}, kSmall{128, 64};
+
+int cols_per_tile(const TileCfg& t, Epi epi) { return epi == Epi::SiluMul ? t.bn / 2 : t.bn; }
+int tiles_of(const TileCfg& t, int M, int Nout, Epi epi) {
+  const int c = cols_per_tile(t, epi);
+  return ((M + t.bm - 1) / t.bm) * ((Nout + c - 1) / c);
+}
+
+// Largest tile that still yields about one workgroup per CU (the 256-row tile
+// only when it is at least half used).
+TileCfg pick_tile(int M, int Nout, Epi epi, int num_cus) {
+  if (M > 128 && tiles_of(kLarge, M, Nout, epi) >= num_cus) return kLarge;
+  if (tiles_of(kMedium, M, Nout, epi) >= num_cus) return kMedium;
+  return kSmall;
+}
+
+template <int BM, int BN, int BK, Epi EPI, AMode MODE>
+hipError_t launch_t(GemvArgs& a, hipStream_t s) {
+  const int num_m = (a.M + BM - 1) / BM;
+  const int cols = EPI == Epi::SiluMul ? BN / 2 : BN;
+  const int num_n = (a.Nout + cols - 1) / cols;
+  const int total = num_m * num_n;
+  const int grid = ((total + 7) / 8) * 8;
+  a.grid_x = num_n;
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, EPI, MODE>), dim3(grid), dim3(256), 0, s, a, num_m, num_n);
+  return hipGetLastError();
+}
+
+template <Epi EPI, AMode MODE>
+hipError_t launch_cfg(GemvArgs& a, int num_cus, hipStream_t s) {
+  const TileCfg t = pick_tile(a.M, a.Nout, EPI, num_cus);
+  if (t.bm == 256) return launch_t<256, 256, 32, EPI, MODE>(a, s);
+  if (t.bn == 128) return launch_t<128, 128, 64, EPI, MODE>(a, s);
+  return launch_t<128, 64, 64, EPI, MODE>(a, s);
+}
+
+}  // namespace
+
+int gemm_parts(int M, int Nout, int num_cus) {
+  const TileCfg t = pick_tile(M, Nout, Epi::Argmax, num_cus);
+  return (Nout + t.bn - 1) / t.bn;
+}
+
+hipError_t launch_gemm(GemvArgs& a, Epi epi, int num_cus, hipStream_t s) {
+  if (a.amode == AMode::Gather) {
+    if (epi == Epi::Store) return launch_cfg<Epi::Store, AMode::Gather>(a, num_cus, s);
+    return hipErrorInvalidValue;
+  }
+  if (a.amode != AMode::Plain) return hipErrorInvalidValue;
+  switch (epi) {
+    case Epi::Store: return launch_cfg<Epi::Store, AMode::Plain>(a, num_cus, s);
+    case Epi::AddTo: return launch_cfg<Epi::AddTo, AMode::Plain>(a, num_cus, s);
+    case Epi::SiluMul: return launch_cfg<Epi::SiluMul, AMode::Plain>(a, num_cus, s);
+    case Epi::QkvRope: return launch_cfg<Epi::QkvRope, AMode::Plain>(a, num_cus, s);
+    case Epi::Argmax: return launch_cfg<Epi::Argmax, AMode::Plain>(a, num_cus, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pe

@@ -2,40 +2,92 @@
 //
 // Y[m, n] = sum_k X[m, k] * W[n, k] where the weights dominate the bytes, so
 // both kernels are organised around reading W exactly once from HBM with
-// 16-byte non-temporal loads and enough of them in flight per CU:
+// 16-byte loads and enough of them in flight per CU:
 //
 // gemv_lds_kernel (M <= 8 per slice, and every fp32 model):
 //   the activation slice is staged once per workgroup in LDS; each wave owns R
 //   consecutive output rows, every lane streams 16-byte pieces of those rows
-//   (two k-steps in flight) and multiplies them with the matching LDS piece of
-//   each activation row (v_dot2_f32_bf16 for bf16).  The R*MT per-lane partial
-//   sums are folded across the wave with a reduce-scatter, so every lane ends
-//   with one finished dot product and applies the epilogue to it.
+//   (two k-steps in flight, non-temporal) and multiplies them with the matching
+//   LDS piece of each activation row (v_dot2_f32_bf16 for bf16).  The R*MT
+//   per-lane partial sums are folded across the wave with a reduce-scatter, so
+//   every lane ends with one finished dot product and applies the epilogue.
 //
 // mfma_skinny_kernel (bf16, 8 < M <= 16 per slice):
 //   at 14-16 rows the VALU would be near saturation at full HBM rate, so the
 //   products run on v_mfma_f32_16x16x32_bf16: the activation rows are the A
-//   operand (one 16-byte piece per lane per k-step, read through the caches)
-//   and 16 weight rows are the B operand, loaded straight from HBM in the MFMA
-//   lane layout.  The SK waves of a workgroup split K, their partial tiles are
-//   summed through LDS and wave 0 applies the epilogue.
+//   operand (one 16-byte piece per lane per k-step) and 16 weight rows are the
+//   B operand, loaded straight from HBM in the MFMA lane layout.  The SK waves
+//   of a workgroup split K, their partial tiles are summed through LDS and
+//   wave 0 applies the epilogue.
 //
-// Epilogues: plain store, residual add, SiLU(gate)*up of paired gate/up rows,
-// and the LM-head argmax, which keeps a running best/runner-up per activation
-// row and writes one candidate per workgroup for a final merge.
+// The activation operand can be formed on the fly (AMode): the fc input
+// concatenation [emb(id) ; h], or RMSNorm of fp32 residual rows whose sums of
+// squares arrive as per-tile partials from the kernel that produced them
+// (Store/AddTo epilogues emit them), so no separate normalisation launch is
+// needed.  Epilogues: store, residual add, SiLU(gate)*up, LM-head argmax
+// candidates, and q/k/v with RoPE and the paged KV write.
 #include "common.h"
 
 namespace pe {
 namespace {
 
+// 1 / sqrt(sum_t ss[t * ld + r] / K + eps), reduced over `lanes` lanes of a wave
+__device__ __forceinline__ float inv_rms_of(const GemvArgs& a, int r, int lane_in, int lanes) {
+  float s = 0.f;
+  for (int t = lane_in; t < a.ss_tiles; t += lanes) s += a.ss[static_cast<int64_t>(t) * a.ss_ld + r];
+  for (int off = lanes / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  return 1.f / sqrtf(s / static_cast<float>(a.K) + a.eps);
+}
+
+// 16 bytes of activation row m starting at element kv * VE, formed per AMode.
+template <typename TW, AMode MODE>
+__device__ __forceinline__ u32x4 load_a16(const GemvArgs& a, int m, int kv, float inv) {
+  constexpr int VE = Elem<TW>::kVec;
+  if constexpr (MODE == AMode::Plain) {
+    return load16(static_cast<const TW*>(a.x) + static_cast<int64_t>(m) * a.K + kv * VE);
+  } else if constexpr (MODE == AMode::Gather) {
+    const int half = a.K / 2;
+    const int k = kv * VE;
+    if (k < half) return load16(static_cast<const TW*>(a.embed) + static_cast<int64_t>(a.ids[m]) * half + k);
+    return load16(static_cast<const TW*>(a.x2) + static_cast<int64_t>(m) * half + (k - half));
+  } else {
+    const int r = a.rows ? a.rows[m] : m;
+    const float* xr = a.xf + static_cast<int64_t>(r) * a.K + kv * VE;
+    const u32x4 g = load16(static_cast<const TW*>(a.gain) + kv * VE);
+    u32x4 out;
+    if constexpr (VE == 8) {
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(xr);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(xr + 4);
+      const float xs[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t gw = g[e];
+        const float ga = bf16_to_f32(static_cast<bf16_t>(gw & 0xffffu));
+        const float gb = bf16_to_f32(static_cast<bf16_t>(gw >> 16));
+        out[e] = static_cast<uint32_t>(f32_to_bf16(xs[2 * e] * inv * ga)) |
+                 (static_cast<uint32_t>(f32_to_bf16(xs[2 * e + 1] * inv * gb)) << 16);
+      }
+    } else {
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(xr);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t gw = g[e];
+        out[e] = __float_as_uint(x0[e] * inv * __uint_as_float(gw));
+      }
+    }
+    return out;
+  }
+}
+
 // ------------------------------------------------------------------ VALU / LDS
-template <typename TW, int MT, int R, Epi EPI>
+template <typename TW, int MT, int R, Epi EPI, AMode MODE>
 __global__ __launch_bounds__(256) void gemv_lds_kernel(GemvArgs a) {
   constexpr int VE = Elem<TW>::kVec;
   constexpr int NV = R * MT;
   constexpr int SH = 6 - Log2<NV>::value;
   constexpr int RG = (EPI == Epi::SiluMul) ? R / 2 : R;  // output rows per group
   extern __shared__ u32x4 xs[];                            // [MT][K / VE]
+  __shared__ float inv_s[MT];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int K = a.K;
@@ -43,11 +95,19 @@ __global__ __launch_bounds__(256) void gemv_lds_kernel(GemvArgs a) {
   const int m0 = blockIdx.y * MT;
   const int mcount = min(MT, a.M - m0);
   {
-    const char* xb = static_cast<const char*>(a.x) + static_cast<int64_t>(m0) * K * sizeof(TW);
+    if constexpr (MODE == AMode::Norm) {
+      for (int m = wave; m < mcount; m += 4) {
+        const int r = a.rows ? a.rows[m0 + m] : m0 + m;
+        const float inv = inv_rms_of(a, r, lane, 64);
+        if (lane == 0) inv_s[m] = inv;
+      }
+      __syncthreads();
+    }
     const u32x4 zero = {0u, 0u, 0u, 0u};
     for (int v = threadIdx.x; v < MT * KV; v += blockDim.x) {
       const int m = v / KV;
-      xs[v] = m < mcount ? load16(xb + static_cast<int64_t>(v) * 16) : zero;
+      xs[v] = m < mcount ? load_a16<TW, MODE>(a, m0 + m, v - m * KV, MODE == AMode::Norm ? inv_s[m] : 0.f)
+                         : zero;
     }
     __syncthreads();
   }
@@ -144,10 +204,24 @@ __global__ __launch_bounds__(256) void gemv_lds_kernel(GemvArgs a) {
 }
 
 // ------------------------------------------------------------------ MFMA skinny
-template <int SK, int U, Epi EPI>
+// Row of W feeding column c (0..15) of tile t.  For QkvRope a tile holds 8
+// rotary pairs of one head: columns c and c+8 are elements j and j + d/2.
+template <Epi EPI>
+__device__ __forceinline__ int tile_row(const GemvArgs& a, int t, int c) {
+  if constexpr (EPI == Epi::QkvRope) {
+    const int per_head = a.rope.d / 16;
+    const int head = t / per_head, p = t - head * per_head;
+    return head * a.rope.d + 8 * p + (c & 7) + (c >= 8 ? a.rope.d / 2 : 0);
+  } else {
+    return t * 16 + c;
+  }
+}
+
+template <int SK, int U, Epi EPI, AMode MODE>
 __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
   constexpr int NB = EPI == Epi::SiluMul ? 2 : 1;  // B tiles per output tile (gate, up)
   __shared__ f32x4 red[SK][NB][64];
+  __shared__ float inv_s[16];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int K = a.K;
@@ -158,8 +232,19 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
   const int m0 = blockIdx.y * 16;
   const int mrow = m0 + (lane & 15);
   const bool xvalid = mrow < a.M;
-  const char* xp = static_cast<const char*>(a.x) +
-                   (static_cast<int64_t>(min(mrow, a.M - 1)) * K + (lane >> 4) * 8) * 2;
+  const int mclamp = min(mrow, a.M - 1);
+  const int j = lane >> 4;
+  if constexpr (MODE == AMode::Norm) {
+    for (int m = wave; m < 16; m += SK) {
+      if (m0 + m < a.M) {
+        const int r = a.rows ? a.rows[m0 + m] : m0 + m;
+        const float inv = inv_rms_of(a, r, lane, 64);
+        if (lane == 0) inv_s[m] = inv;
+      }
+    }
+    __syncthreads();
+  }
+  const float inv = (MODE == AMode::Norm && xvalid) ? inv_s[lane & 15] : 0.f;
   const int T = (a.Nout + 15) / 16;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   Top2 best[4];
@@ -167,12 +252,11 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
   for (int q = 0; q < 4; ++q) best[q] = top2_empty();
 
   for (int t = blockIdx.x; t < T; t += gridDim.x) {
-    const int n0 = t * 16;
-    const int nrow = min(n0 + (lane & 15), a.Nout - 1);
+    const int nrow = min(tile_row<EPI>(a, t, lane & 15), a.Nout - 1);
     const bf16_t* wp[NB];
     if constexpr (EPI == Epi::SiluMul) {
-      wp[0] = static_cast<const bf16_t*>(a.w_a) + static_cast<int64_t>(nrow) * K + (lane >> 4) * 8;
-      wp[NB - 1] = static_cast<const bf16_t*>(a.w_b) + static_cast<int64_t>(nrow) * K + (lane >> 4) * 8;
+      wp[0] = static_cast<const bf16_t*>(a.w_a) + static_cast<int64_t>(nrow) * K + j * 8;
+      wp[NB - 1] = static_cast<const bf16_t*>(a.w_b) + static_cast<int64_t>(nrow) * K + j * 8;
     } else {
       const bf16_t* base;
       int rr;
@@ -186,7 +270,7 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
         base = static_cast<const bf16_t*>(a.w_c);
         rr = nrow - a.n_a - a.n_b;
       }
-      wp[0] = base + static_cast<int64_t>(rr) * K + (lane >> 4) * 8;
+      wp[0] = base + static_cast<int64_t>(rr) * K + j * 8;
     }
     f32x4 acc[NB];
 #pragma unroll
@@ -197,8 +281,8 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
       for (int u = 0; u < U; ++u) {
         const bool ok = s + u < ks1;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) bv[u][b] = ok ? load16_stream(wp[b] + (s + u) * 32) : zero;
-        av[u] = (ok && xvalid) ? load16(xp + (s + u) * 64) : zero;
+        for (int b = 0; b < NB; ++b) bv[u][b] = ok ? load16(wp[b] + (s + u) * 32) : zero;
+        av[u] = (ok && xvalid) ? load_a16<bf16_t, MODE>(a, mclamp, 4 * (s + u) + j, inv) : zero;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -218,22 +302,81 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
 #pragma unroll
         for (int w = 1; w < SK; ++w) sum[b] += red[w][b][lane];
       }
-      const int n = n0 + (lane & 15);
+      const int c = lane & 15;
+      const int n = tile_row<EPI>(a, t, c);
+      if constexpr (EPI == Epi::Store || EPI == Epi::AddTo) {
+        float sq[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = m0 + 4 * (lane >> 4) + q;
-        if (m >= a.M || n >= a.Nout) continue;
-        const float v = sum[0][q];
-        if constexpr (EPI == Epi::Store) {
-          a.y[static_cast<int64_t>(m) * a.ldy + n] = v;
-        } else if constexpr (EPI == Epi::AddTo) {
-          a.y[static_cast<int64_t>(m) * a.ldy + n] += v;
-        } else if constexpr (EPI == Epi::SiluMul) {
-          const float s = v / (1.f + expf(-v));
-          static_cast<bf16_t*>(a.y_op)[static_cast<int64_t>(m) * a.ldy + n] = f32_to_bf16(s * sum[NB - 1][q]);
-        } else {
+        for (int q = 0; q < 4; ++q) {
+          const int m = m0 + 4 * j + q;
+          float v = sum[0][q];
+          sq[q] = 0.f;
+          if (m < a.M && n < a.Nout) {
+            float* y = a.y + static_cast<int64_t>(m) * a.ldy + n;
+            if constexpr (EPI == Epi::AddTo) v += *y;
+            *y = v;
+            sq[q] = v * v;
+          }
+        }
+        if (a.ss_out) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) sq[q] += __shfl_xor(sq[q], off, 64);
+            const int m = m0 + 4 * j + q;
+            if (c == 0 && m < a.M) a.ss_out[static_cast<int64_t>(t) * a.M + m] = sq[q];
+          }
+        }
+      } else if constexpr (EPI == Epi::SiluMul) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = m0 + 4 * j + q;
+          if (m >= a.M || n >= a.Nout) continue;
+          const float v = sum[0][q];
+          const float sg = v / (1.f + expf(-v));
+          static_cast<bf16_t*>(a.y_op)[static_cast<int64_t>(m) * a.ldy + n] = f32_to_bf16(sg * sum[NB - 1][q]);
+        }
+      } else if constexpr (EPI == Epi::Argmax) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = m0 + 4 * j + q;
+          if (m >= a.M || n >= a.Nout) continue;
+          const float v = sum[0][q];
           if (a.logits) a.logits[static_cast<int64_t>(m) * a.Nout + n] = v;
           top2_push(best[q], v, n);
+        }
+      } else {  // QkvRope
+        const RopeOut& ro = a.rope;
+        const int d = ro.d;
+        const int head = n / d;
+        const int e = n - head * d;                  // element within the head
+        const int jj = e % (d / 2);                  // rotary pair index
+        const bool rotate = head < ro.n_q + ro.n_kv;
+        const double inv_freq = ro.freq.inv[jj];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = m0 + 4 * j + q;
+          const float v = sum[0][q];
+          const float partner = __shfl_xor(v, 8, 64);
+          if (m >= a.M || ro.rejected[m]) continue;
+          float out = v;
+          if (rotate) {
+            float cs, sn;
+            rope_cos_sin(ro.pos[m], inv_freq, cs, sn);
+            out = c < 8 ? v * cs - partner * sn : v * cs + partner * sn;
+          }
+          if (head < ro.n_q) {
+            static_cast<bf16_t*>(ro.q_out)[(static_cast<int64_t>(m) * ro.n_q + head) * d + e] = f32_to_bf16(out);
+          } else {
+            const int64_t slot = ro.slot[m];
+            if (slot < 0) continue;
+            const bool is_k = head < ro.n_q + ro.n_kv;
+            const int g = is_k ? head - ro.n_q : head - ro.n_q - ro.n_kv;
+            const int64_t blk = slot / ro.block_size;
+            const int off = static_cast<int>(slot - blk * ro.block_size);
+            static_cast<bf16_t*>(is_k ? ro.k_cache : ro.v_cache)[((blk * ro.n_kv + g) * ro.block_size + off) * d + e] =
+                f32_to_bf16(out);
+          }
         }
       }
     }
@@ -253,7 +396,7 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
           o.pad = 0;
           best[q] = top2_merge(best[q], o);
         }
-        const int m = m0 + 4 * (lane >> 4) + q;
+        const int m = m0 + 4 * j + q;
         if ((lane & 15) == 0 && m < a.M) a.partials[static_cast<int64_t>(m) * gridDim.x + blockIdx.x] = best[q];
       }
     }
@@ -267,68 +410,80 @@ int gemv_m_tile(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 
 
 bool use_mfma(int M, int K, DType dt) { return dt == DType::BF16 && M > 8 && K % 32 == 0; }
 
-int skinny_sk(int K) { return K >= 4096 ? 8 : 4; }
+// Waves per workgroup for the MFMA kernel: enough that each wave's share of
+// K fits in one batch of U_SKINNY k-steps (all its loads in flight at once).
+// Paired gate/up tiles, the argmax state and the RoPE epilogue need more
+// registers: at most 8 waves there.
+constexpr int U_SKINNY = 12;
+int skinny_sk(int K, Epi epi) {
+  const int ks = K / 32;
+  const int sk = ks <= 4 * U_SKINNY ? 4 : ks <= 8 * U_SKINNY ? 8 : 16;
+  return (epi == Epi::Store || epi == Epi::AddTo) ? sk : (sk > 8 ? 8 : sk);
+}
 
-template <typename TW, int MT, int R, Epi EPI>
+template <Epi EPI, AMode MODE>
+hipError_t launch_mfma(GemvArgs& a, int num_cus, hipStream_t s) {
+  const int T = (a.Nout + 15) / 16;
+  const int gx = T < num_cus * 4 ? T : num_cus * 4;
+  a.grid_x = gx;
+  dim3 grid(gx, (a.M + 15) / 16);
+  switch (skinny_sk(a.K, EPI)) {
+    case 16:
+      if constexpr (EPI == Epi::Store || EPI == Epi::AddTo)
+        hipLaunchKernelGGL((mfma_skinny_kernel<16, U_SKINNY, EPI, MODE>), grid, dim3(1024), 0, s, a);
+      break;
+    case 8: hipLaunchKernelGGL((mfma_skinny_kernel<8, U_SKINNY, EPI, MODE>), grid, dim3(512), 0, s, a); break;
+    default: hipLaunchKernelGGL((mfma_skinny_kernel<4, U_SKINNY, EPI, MODE>), grid, dim3(256), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+template <typename TW, int MT, int R, Epi EPI, AMode MODE>
 hipError_t launch_lds(GemvArgs& a, dim3 grid, hipStream_t s) {
   const size_t lds = static_cast<size_t>(MT) * a.K * sizeof(TW);
   static bool raised = false;
   if (lds > 64 * 1024 && !raised) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_lds_kernel<TW, MT, R, EPI>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_lds_kernel<TW, MT, R, EPI, MODE>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
       return hipErrorInvalidValue;
     raised = true;
   }
-  hipLaunchKernelGGL((gemv_lds_kernel<TW, MT, R, EPI>), grid, dim3(256), lds, s, a);
+  hipLaunchKernelGGL((gemv_lds_kernel<TW, MT, R, EPI, MODE>), grid, dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
-template <typename TW, Epi EPI>
-hipError_t launch_typed(GemvArgs& a, int num_cus, hipStream_t s) {
-  if (use_mfma(a.M, a.K, sizeof(TW) == 2 ? DType::BF16 : DType::F32)) {
-    if constexpr (sizeof(TW) == 2) {
-      const int T = (a.Nout + 15) / 16;
-      int gx = T < num_cus * 4 ? T : num_cus * 4;
-      a.grid_x = gx;
-      dim3 grid(gx, (a.M + 15) / 16);
-      if (skinny_sk(a.K) == 8)
-        hipLaunchKernelGGL((mfma_skinny_kernel<8, 8, EPI>), grid, dim3(512), 0, s, a);
-      else
-        hipLaunchKernelGGL((mfma_skinny_kernel<4, 8, EPI>), grid, dim3(256), 0, s, a);
-      return hipGetLastError();
-    }
-  }
+template <typename TW, Epi EPI, AMode MODE>
+hipError_t launch_valu(GemvArgs& a, int num_cus, hipStream_t s) {
   const int m_tile = gemv_m_tile(a.M);
   const int R = m_tile >= 16 ? 4 : m_tile >= 8 ? 8 : 16;  // R * MT <= 64
   const int rg = EPI == Epi::SiluMul ? R / 2 : R;
   const int groups = (a.Nout + rg - 1) / rg;
   int gx = (groups + 3) / 4;
-  if (gx > num_cus) gx = num_cus;
+  if (gx > 2 * num_cus) gx = 2 * num_cus;
   if (gx < 1) gx = 1;
   a.grid_x = gx;
   dim3 grid(gx, (a.M + m_tile - 1) / m_tile);
   switch (m_tile) {
-    case 16: return launch_lds<TW, 16, 4, EPI>(a, grid, s);
-    case 8: return launch_lds<TW, 8, 8, EPI>(a, grid, s);
-    case 4: return launch_lds<TW, 4, 16, EPI>(a, grid, s);
-    case 2: return launch_lds<TW, 2, 16, EPI>(a, grid, s);
-    default: return launch_lds<TW, 1, 16, EPI>(a, grid, s);
-  }
-}
-
-template <typename TW>
-hipError_t launch_dtype(GemvArgs& a, Epi epi, int num_cus, hipStream_t s) {
-  switch (epi) {
-    case Epi::Store: return launch_typed<TW, Epi::Store>(a, num_cus, s);
-    case Epi::AddTo: return launch_typed<TW, Epi::AddTo>(a, num_cus, s);
-    case Epi::SiluMul: return launch_typed<TW, Epi::SiluMul>(a, num_cus, s);
-    default: return launch_typed<TW, Epi::Argmax>(a, num_cus, s);
+    case 16: return launch_lds<TW, 16, 4, EPI, MODE>(a, grid, s);
+    case 8: return launch_lds<TW, 8, 8, EPI, MODE>(a, grid, s);
+    case 4: return launch_lds<TW, 4, 16, EPI, MODE>(a, grid, s);
+    case 2: return launch_lds<TW, 2, 16, EPI, MODE>(a, grid, s);
+    default: return launch_lds<TW, 1, 16, EPI, MODE>(a, grid, s);
   }
 }
 
 }  // namespace
 
+ProjKernel proj_kernel(int M, int K, DType dt) {
+  if (dt == DType::BF16 && M > 16 && K % 64 == 0) return ProjKernel::Tiled;
+  if (use_mfma(M, K, dt)) return ProjKernel::Skinny;
+  return ProjKernel::Lds;
+}
+
+bool gemv_uses_mfma(int M, int K, DType dt) { return proj_kernel(M, K, dt) != ProjKernel::Lds; }
+
 int gemv_grid_x(int M, int Nout, Epi epi, DType dt, int num_cus, int K) {
+  if (proj_kernel(M, K, dt) == ProjKernel::Tiled) return gemm_parts(M, Nout, num_cus);
   if (use_mfma(M, K, dt)) {
     const int T = (Nout + 15) / 16;
     return T < num_cus * 4 ? T : num_cus * 4;
@@ -337,18 +492,64 @@ int gemv_grid_x(int M, int Nout, Epi epi, DType dt, int num_cus, int K) {
   const int R = m_tile >= 16 ? 4 : m_tile >= 8 ? 8 : 16;
   const int rg = epi == Epi::SiluMul ? R / 2 : R;
   int gx = ((Nout + rg - 1) / rg + 3) / 4;
-  if (gx > num_cus) gx = num_cus;
+  if (gx > 2 * num_cus) gx = 2 * num_cus;
   return gx < 1 ? 1 : gx;
 }
 
 size_t gemv_lds_bytes(int M, int K, DType dt) {
-  if (use_mfma(M, K, dt)) return 0;
+  if (proj_kernel(M, K, dt) != ProjKernel::Lds) return 0;
   return static_cast<size_t>(gemv_m_tile(M)) * K * elem_bytes(dt);
 }
 
+// Supported (epilogue, operand) pairs: every epilogue with a plain operand on
+// the MFMA kernel (QkvRope only there), every epilogue but QkvRope with a plain
+// operand on the LDS kernel; the fused forms Store+Gather (fc), QkvRope+Norm,
+// SiluMul+Norm and Argmax+Norm on the MFMA kernel, Argmax+Norm on the LDS kernel.
 hipError_t launch_gemv(GemvArgs& a, Epi epi, DType dt, int num_cus, hipStream_t s) {
-  if (dt == DType::F32) return launch_dtype<float>(a, epi, num_cus, s);
-  return launch_dtype<bf16_t>(a, epi, num_cus, s);
+  if (proj_kernel(a.M, a.K, dt) == ProjKernel::Tiled) return launch_gemm(a, epi, num_cus, s);
+  if (use_mfma(a.M, a.K, dt)) {
+    if (a.amode == AMode::Plain) {
+      switch (epi) {
+        case Epi::Store: return launch_mfma<Epi::Store, AMode::Plain>(a, num_cus, s);
+        case Epi::AddTo: return launch_mfma<Epi::AddTo, AMode::Plain>(a, num_cus, s);
+        case Epi::SiluMul: return launch_mfma<Epi::SiluMul, AMode::Plain>(a, num_cus, s);
+        case Epi::Argmax: return launch_mfma<Epi::Argmax, AMode::Plain>(a, num_cus, s);
+        case Epi::QkvRope: return launch_mfma<Epi::QkvRope, AMode::Plain>(a, num_cus, s);
+      }
+      return hipErrorInvalidValue;
+    }
+    if (a.amode == AMode::Gather && epi == Epi::Store) return launch_mfma<Epi::Store, AMode::Gather>(a, num_cus, s);
+    if (a.amode == AMode::Norm) {
+      switch (epi) {
+        case Epi::QkvRope: return launch_mfma<Epi::QkvRope, AMode::Norm>(a, num_cus, s);
+        case Epi::SiluMul: return launch_mfma<Epi::SiluMul, AMode::Norm>(a, num_cus, s);
+        case Epi::Argmax: return launch_mfma<Epi::Argmax, AMode::Norm>(a, num_cus, s);
+        default: return hipErrorInvalidValue;
+      }
+    }
+    return hipErrorInvalidValue;
+  }
+  if (a.amode == AMode::Plain) {
+    switch (epi) {
+      case Epi::Store:
+        return dt == DType::F32 ? launch_valu<float, Epi::Store, AMode::Plain>(a, num_cus, s)
+                                : launch_valu<bf16_t, Epi::Store, AMode::Plain>(a, num_cus, s);
+      case Epi::AddTo:
+        return dt == DType::F32 ? launch_valu<float, Epi::AddTo, AMode::Plain>(a, num_cus, s)
+                                : launch_valu<bf16_t, Epi::AddTo, AMode::Plain>(a, num_cus, s);
+      case Epi::SiluMul:
+        return dt == DType::F32 ? launch_valu<float, Epi::SiluMul, AMode::Plain>(a, num_cus, s)
+                                : launch_valu<bf16_t, Epi::SiluMul, AMode::Plain>(a, num_cus, s);
+      case Epi::Argmax:
+        return dt == DType::F32 ? launch_valu<float, Epi::Argmax, AMode::Plain>(a, num_cus, s)
+                                : launch_valu<bf16_t, Epi::Argmax, AMode::Plain>(a, num_cus, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (a.amode == AMode::Norm && epi == Epi::Argmax)
+    return dt == DType::F32 ? launch_valu<float, Epi::Argmax, AMode::Norm>(a, num_cus, s)
+                            : launch_valu<bf16_t, Epi::Argmax, AMode::Norm>(a, num_cus, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pe

@@ -19,6 +19,12 @@ struct Top2 {
 
 inline int elem_bytes(DType t) { return t == DType::F32 ? 4 : 2; }
 
+// Rotary inverse frequencies theta^(-2j/d), j < d/2 <= 64, formed on the host in
+// double precision and passed by value in the kernel arguments.
+struct RopeFreq {
+  double inv[64];
+};
+
 // ---------------------------------------------------------------- expansion
 struct PrepareArgs {
   int c, K, T, N, H, block_size, max_blocks, mask_id;
@@ -33,29 +39,68 @@ struct PrepareArgs {
 };
 hipError_t launch_prepare(const PrepareArgs& a, hipStream_t s);
 
-// ---------------------------------------------------------------- GEMV (skinny GEMM)
-enum class Epi { Store = 0, AddTo = 1, SiluMul = 2, Argmax = 3 };
+// ---------------------------------------------------------------- projections
+enum class Epi { Store = 0, AddTo = 1, SiluMul = 2, Argmax = 3, QkvRope = 4 };
+
+// How the activation operand X[m, :] is formed.
+enum class AMode {
+  Plain = 0,   // X = x[m], model dtype, row stride K
+  Gather = 1,  // X = [embed[ids[m]] ; x2[m]], each half K/2 elements (fc input)
+  Norm = 2     // X = round(xf[r] / sqrt(mean(xf[r]^2) + eps) * gain), r = rows ? rows[m] : m;
+               //     sum of xf[r]^2 = sum over t < ss_tiles of ss[t * ss_ld + r]
+};
+
+// Outputs of the fused q/k/v projection: rotate-half RoPE of q and k at the
+// row's position, q stored as the attention operand, k/v written to the paged
+// cache at the row's slot (nothing for slot -1).
+struct RopeOut {
+  int n_q, n_kv, d, block_size;
+  RopeFreq freq;
+  const int32_t* pos;
+  const int64_t* slot;
+  const uint8_t* rejected;
+  void* q_out;                 // [M, n_q * d] model dtype
+  void *k_cache, *v_cache;     // [blocks, n_kv, block_size, d]
+};
 
 struct GemvArgs {
   // Y[m, n] = sum_k X[m, k] * W[n, k] for m < M, n < Nout.
   int M, Nout, K;
-  const void* x;          // operand rows [M, K], model dtype, row stride K
+  AMode amode;
+  const void* x;               // Plain
+  const int32_t* ids;          // Gather
+  const void *embed, *x2;      // Gather
+  const float* xf;             // Norm
+  const int32_t* rows;         // Norm (optional row gather)
+  const void* gain;            // Norm
+  const float* ss;             // Norm
+  int ss_tiles, ss_ld;         // Norm
+  float eps;                   // Norm
   // W rows: [0, n_a) from w_a, [n_a, n_a + n_b) from w_b, the rest from w_c;
   // every W row has K elements.  For Epi::SiluMul, w_a is the gate and w_b the
   // up projection (both Nout rows).
   const void *w_a, *w_b, *w_c;
   int n_a, n_b;
   // outputs
-  float* y;               // Store / AddTo: fp32 [M, ldy]
-  void* y_op;             // SiluMul: model dtype [M, ldy]
+  float* y;                    // Store / AddTo: fp32 [M, ldy]
+  void* y_op;                  // SiluMul: model dtype [M, ldy]
   int ldy;
-  float* logits;          // Argmax: optional fp32 [M, Nout]
-  Top2* partials;         // Argmax: [M, gridDim.x]
-  int grid_x;             // filled by the launcher
+  float* ss_out;               // Store / AddTo (MFMA kernel): [Nout / 16, M] row sums of y^2 per 16-column tile
+  float* logits;               // Argmax: optional fp32 [M, Nout]
+  Top2* partials;              // Argmax: [M, grid_x]
+  RopeOut rope;                // QkvRope
+  int grid_x;                  // filled by the launcher
 };
+// Kernel families: LDS-staged dot2 GEMV (M <= 8 per slice, fp32), weight-streaming
+// MFMA (bf16, 8 < M <= 16), tiled MFMA GEMM (bf16, M > 16, K % 64 == 0).
+enum class ProjKernel { Lds = 0, Skinny = 1, Tiled = 2 };
+ProjKernel proj_kernel(int M, int K, DType dt);
+hipError_t launch_gemm(GemvArgs& a, Epi epi, int num_cus, hipStream_t s);
+int gemm_parts(int M, int Nout, int num_cus);  // argmax candidates per row of the tiled kernel
 hipError_t launch_gemv(GemvArgs& a, Epi epi, DType dt, int num_cus, hipStream_t s);
 int gemv_grid_x(int M, int Nout, Epi epi, DType dt, int num_cus, int K);
 size_t gemv_lds_bytes(int M, int K, DType dt);  // dynamic LDS of the chosen kernel
+bool gemv_uses_mfma(int M, int K, DType dt);
 
 // ---------------------------------------------------------------- small kernels
 hipError_t launch_build_fc_input(DType dt, int N, int H, const int32_t* ids, const void* embed,
@@ -65,7 +110,7 @@ hipError_t launch_rmsnorm(DType dt, int rows, int H, const int32_t* row_idx, con
 
 struct RopeArgs {
   int N, n_q, n_kv, d, block_size;
-  float theta;
+  RopeFreq freq;
   DType dtype;
   const float* qkv;             // [N, (n_q + 2 n_kv) d]
   const int32_t* pos;

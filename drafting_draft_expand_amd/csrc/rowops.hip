@@ -54,8 +54,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int H, const int32_t* __re
 // Rotate-half RoPE of q and k at the row's position, q stored as the attention
 // operand, k and v written to the paged cache at the row's slot.  Rows with
 // slot -1 (rejected, "P-EAGLE: Parallel Speculative Decoding in vLLM", KV Cache
-// and CUDA Graphs) write nothing.  Angles are formed in double precision so
-// that large positions keep full fp32 accuracy in cos/sin.
+// and CUDA Graphs) write nothing.
 template <typename T>
 __global__ __launch_bounds__(256) void rope_kv_kernel(RopeArgs a) {
   const int r = blockIdx.x;
@@ -69,11 +68,8 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeArgs a) {
   const float* src = a.qkv + static_cast<int64_t>(r) * heads * a.d + head * a.d;
   float x1 = src[j], x2 = src[j + half];
   if (head < a.n_q + a.n_kv) {
-    const double inv = pow(static_cast<double>(a.theta), -2.0 * j / a.d);
-    const double ang = static_cast<double>(a.pos[r]) * inv;
-    double sd, cd;
-    sincos(ang, &sd, &cd);
-    const float c = static_cast<float>(cd), s = static_cast<float>(sd);
+    float c, s;
+    rope_cos_sin(a.pos[r], a.freq.inv[j], c, s);
     const float y1 = x1 * c - x2 * s;
     const float y2 = x2 * c + x1 * s;
     x1 = y1;

@@ -143,6 +143,14 @@ def test_forward_head_dims(dtype, d):
     _forward_case(wl)
 
 
+def test_forward_bf16_few_rows_unfused():
+    """c=1, K=3: 6 draft rows, so every projection takes the VALU path with the
+    separate gather / norm / RoPE kernels."""
+    spec = synth.ModelSpec(hidden=256, vocab=1000, n_layers=1, n_q=8, n_kv=2, head_dim=64, inter=512)
+    wl = synth.Workload("few-rows-bf16", spec, c=1, K=3, ctx_lo=30, ctx_hi=90, accept_hi=3, seed=43)
+    _forward_case(wl)
+
+
 def test_forward_small_bf16():
     spec = synth.ModelSpec(hidden=256, vocab=1000, n_layers=1, n_q=8, n_kv=2, head_dim=64, inter=512)
     wl = synth.Workload("small-bf16", spec, c=6, K=5, ctx_lo=10, ctx_hi=300, accept_hi=5, seed=41)
