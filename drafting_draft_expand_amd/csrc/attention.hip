@@ -163,8 +163,10 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   constexpr int KK = D / 32;   // k-steps of S^T
   constexpr int PER = KT * D / 8 / 512;  // 16-byte K (and V) pieces per thread per tile
   static_assert(PER >= 1, "tile too small for the workgroup");
+  constexpr int MAXB = 1024;   // pages of one split held in LDS
   __shared__ bf16_t ks[KT * KP];
   __shared__ bf16_t vt[D * VP];
+  __shared__ int32_t pages[MAXB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, j = lane >> 4;
   const int sp = blockIdx.x, g = blockIdx.y, i = blockIdx.z;
   const int grp = a.n_q / a.n_kv;
@@ -181,8 +183,15 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   const bf16_t* vc = static_cast<const bf16_t*>(a.v_cache);
   const int32_t* bt = a.block_table + static_cast<int64_t>(i) * a.max_blocks;
   const u32x4 zero = {0u, 0u, 0u, 0u};
+  // the split's page numbers, so K/V addresses do not wait on a table load
+  const int pg0 = kb / a.block_size;
+  const int npg = ke > kb ? (ke - 1) / a.block_size - pg0 + 1 : 0;
+  const bool paged_lds = npg <= MAXB;
+  for (int q = tid; q < npg && paged_lds; q += 512) pages[q] = bt[pg0 + q];
+  __syncthreads();
 
-  u32x4 kr[2][PER], vr[2][PER];
+  constexpr int DEPTH = 3;  // tiles in flight
+  u32x4 kr[DEPTH][PER], vr[DEPTH][PER];
   auto fetch = [&](int t, int set) {
 #pragma unroll
     for (int pp = 0; pp < PER; ++pp) {
@@ -192,7 +201,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
       kr[set][pp] = zero;
       vr[set][pp] = zero;
       if (p < ke) {
-        const int64_t blk = bt[p / a.block_size];
+        const int64_t blk = paged_lds ? pages[p / a.block_size - pg0] : bt[p / a.block_size];
         const int64_t off = ((blk * a.n_kv + g) * a.block_size + p % a.block_size) * D + c8 * 8;
         kr[set][pp] = load16(kc + off);
         vr[set][pp] = load16(vc + off);
@@ -229,14 +238,16 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int t = 0; t < DT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (ntiles > 0) fetch(0, 0);
-    if (ntiles > 1) fetch(1, 1);
+#pragma unroll
+    for (int t = 0; t < DEPTH; ++t)
+      if (t < ntiles) fetch(t, t);
     for (int t = 0; t < ntiles; ++t) {
       const int kt0 = kb + t * KT;
+      const int set = t % DEPTH;
       __syncthreads();
-      stash(t & 1);
+      stash(set);
       __syncthreads();
-      if (t + 2 < ntiles) fetch(t + 2, t & 1);
+      if (t + DEPTH < ntiles) fetch(t + DEPTH, set);
 
       f32x4 st[4];
 #pragma unroll

@@ -4,12 +4,12 @@
 // C[m, n] = sum_k A[m, k] * W[n, k], A and W both row-major with K contiguous.
 // Four waves in a 2 x 2 grid per workgroup; each wave owns a WM x WN block of
 // v_mfma_f32_16x16x32_bf16 tiles.  Per K step the next A/W tiles are fetched
-// into registers while the current ones are read from LDS (rows padded by 16
-// bytes so the 16-row fragment reads spread over the banks), then written to
-// the other LDS buffer: one barrier per K step.  LDS traffic per MFMA falls as
-// the wave block grows, so the largest tile that still gives every CU work
-// is chosen: 256 x 256 (128 x 128 per wave, 256 accumulator registers) for the
-// LM head, smaller ones for the layer projections.
+// into registers while the current ones are read from LDS (16-byte chunks
+// XOR-swizzled within each row, so fragment reads and staging writes are free
+// of bank conflicts), then written to the other LDS buffer: one barrier per K
+// step.  LDS traffic per MFMA falls as the wave block grows, so the largest
+// tile that still gives every CU work is chosen: 128 x 256 (64 x 128 per
+// wave) for the LM head and wide projections, smaller ones otherwise.
 //
 // Tile order is XCD-aware: workgroups are dealt round-robin to the 8 XCDs, so
 // the logical tile index is taken from (blockIdx % 8, blockIdx / 8) such that
@@ -21,6 +21,8 @@
 // q/k/v with RoPE and the paged KV write (each 16-column MFMA tile holds 8
 // rotary pairs, columns c and c^8), and LM-head argmax candidates per
 // (row, 256-column tile).
+#include <type_traits>
+
 #include "common.h"
 
 namespace pe {
@@ -58,6 +60,17 @@ __device__ __forceinline__ const bf16_t* b_ptr(const GemvArgs& a, int nt, int r)
   }
 }
 
+// Element offset of 16-byte chunk c of LDS tile row r (rows of CPR chunks,
+// unpadded).  Chunks are XOR-swizzled within the row -- c ^ (r & 7) for
+// 128-byte rows, c ^ ((r >> 1) & 3) for 64-byte rows -- so that both the
+// staging writes (consecutive lanes along a row) and the MFMA fragment reads
+// (16 rows, 4 chunks) of ds_read_b128 / ds_write_b128 hit distinct banks.
+template <int CPR>
+__device__ __forceinline__ int lds_off(int r, int c) {
+  const int sw = CPR == 8 ? (c ^ (r & 7)) : (c ^ ((r >> 1) & 3));
+  return r * (CPR * 8) + sw * 8;
+}
+
 template <AMode MODE>
 __device__ __forceinline__ u32x4 a_load(const GemvArgs& a, int m, int k) {
   if constexpr (MODE == AMode::Gather) {
@@ -69,92 +82,16 @@ __device__ __forceinline__ u32x4 a_load(const GemvArgs& a, int m, int k) {
   }
 }
 
-template <int BM, int BN, int BK, Epi EPI, AMode MODE>
-__global__ __launch_bounds__(256) void gemm_kernel(GemvArgs a, int num_m, int num_n) {
-  constexpr int WM = BM / 2, WN = BN / 2;     // wave block
-  constexpr int TM = WM / 16, TN = WN / 16;   // MFMA tiles per wave
-  constexpr int LDT = BK + 8;                 // padded LDS row, elements
-  constexpr int CPR = BK / 8;                 // 16-byte chunks per tile row
-  constexpr int NA = BM * CPR / 256, NB = BN * CPR / 256;  // chunks per thread
-  static_assert(NA >= 1 && NB >= 1, "tile too small");
-  __shared__ bf16_t As[2][BM * LDT];
-  __shared__ bf16_t Bs[2][BN * LDT];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
-  // XCD-aware tile order: the M tiles of one W tile land on one XCD
-  const int total = num_m * num_n;
-  const int per_xcd = (total + 7) / 8;
-  const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (L >= total) return;
-  const int mt = L % num_m, nt = L / num_m;
-  const int m0 = mt * BM;
-  const int nk = a.K / BK;
-
-  const bf16_t* bp[NB];
-  int a_row[NA], a_col[NA], b_r[NB], b_col[NB];
-#pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int c = tid + 256 * i;
-    a_row[i] = c / CPR;
-    a_col[i] = (c % CPR) * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int c = tid + 256 * i;
-    b_r[i] = c / CPR;
-    b_col[i] = (c % CPR) * 8;
-    bp[i] = b_ptr<EPI, BN, WN>(a, nt, b_r[i]) + b_col[i];
-  }
-  u32x4 ra[NA], rb[NB];
-  auto fetch = [&](int kt) {
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < NA; ++i) ra[i] = a_load<MODE>(a, min(m0 + a_row[i], a.M - 1), k0 + a_col[i]);
-#pragma unroll
-    for (int i = 0; i < NB; ++i) rb[i] = load16(bp[i] + k0);
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NA; ++i) store16(&As[buf][a_row[i] * LDT + a_col[i]], ra[i]);
-#pragma unroll
-    for (int i = 0; i < NB; ++i) store16(&Bs[buf][b_r[i] * LDT + b_col[i]], rb[i]);
-  };
-
-  f32x4 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int jn = 0; jn < TN; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  fetch(0);
-  stash(0);
-  __syncthreads();
+// Epilogue of one output tile held in MFMA accumulators: wave (wm, wn) of a
+// WGM x WGN wave grid owns rows m0 + wm * 16 TM .. and tile columns
+// wn * 16 TN ..; lane l holds rows 4 (l / 16) + q, column l % 16 of each
+// 16 x 16 block.  red is LDS scratch for WGN * BM candidates (argmax only).
+template <int BM, int BN, int WGM, int WGN, int TM, int TN, Epi EPI>
+__device__ __forceinline__ void tile_epilogue(const GemvArgs& a, f32x4 (&acc)[TM][TN], int m0, int nt, int num_n,
+                                              int wm, int wn, Top2* red) {
+  constexpr int WM = TM * 16, WN = TN * 16, NT = WGM * WGN * 64;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int l16 = lane & 15, lq = lane >> 4;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) fetch(kt + 1);
-#pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      u32x4 af[TM], bf[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const u32x4*>(&As[cur][(wm * WM + i * 16 + l16) * LDT + ks * 32 + lq * 8]);
-#pragma unroll
-      for (int jn = 0; jn < TN; ++jn)
-        bf[jn] = *reinterpret_cast<const u32x4*>(&Bs[cur][(wn * WN + jn * 16 + l16) * LDT + ks * 32 + lq * 8]);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int jn = 0; jn < TN; ++jn)
-          acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[i]),
-                                                               __builtin_bit_cast(bf16x8, bf[jn]), acc[i][jn], 0, 0,
-                                                               0);
-    }
-    if (kt + 1 < nk) stash(cur ^ 1);
-    __syncthreads();
-  }
-
-  // ---------------------------------------------------------------- epilogue
   if constexpr (EPI == Epi::Store || EPI == Epi::AddTo) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -226,8 +163,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemvArgs a, int num_m, int nu
         }
     }
   } else {  // Argmax over this tile's BN columns, per row
-    Top2* red = reinterpret_cast<Top2*>(&As[0][0]);  // [2 wave columns][BM rows]
-    static_assert(2 * BM * sizeof(Top2) <= sizeof(As) / 2, "argmax scratch must fit one LDS buffer");
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -255,18 +190,147 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemvArgs a, int num_m, int nu
         if (l16 == 0) red[wn * BM + wm * WM + i * 16 + lq * 4 + q] = t;
       }
     __syncthreads();
-    for (int r = tid; r < BM; r += 256) {
+    for (int r = tid; r < BM; r += NT) {
       const int m = m0 + r;
-      if (m < a.M) a.partials[static_cast<int64_t>(m) * num_n + nt] = top2_merge(red[r], red[BM + r]);
+      Top2 t = red[r];
+#pragma unroll
+      for (int w = 1; w < WGN; ++w) t = top2_merge(t, red[w * BM + r]);
+      if (m < a.M) a.partials[static_cast<int64_t>(m) * num_n + nt] = t;
     }
   }
 }
 
-// Tile shapes: {BM, BN, BK}.
+template <int BM, int BN, int BK, int PD, int WGM, Epi EPI, AMode MODE>
+__global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel(GemvArgs a, int num_m, int num_n) {
+  constexpr int WGN = 4 / WGM;                // wave grid WGM x WGN
+  constexpr int WM = BM / WGM, WN = BN / WGN; // wave block
+  constexpr int TM = WM / 16, TN = WN / 16;   // MFMA tiles per wave
+  constexpr int LDT = BK;                     // LDS row, elements (no padding: chunks are swizzled)
+  constexpr int CPR = BK / 8;                 // 16-byte chunks per tile row
+  static_assert(CPR == 4 || CPR == 8, "K step 32 or 64");
+  constexpr int NA = (BM * CPR + 255) / 256, NB = (BN * CPR + 255) / 256;  // chunks per thread
+  static_assert(NA >= 1 && NB >= 1, "tile too small");
+  static_assert(PD == 1 || PD == 2, "prefetch distance 1 or 2");
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * LDT];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * LDT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WGM, wn = wave / WGM;
+  // XCD-aware tile order: the M tiles of one W tile land on one XCD
+  const int total = num_m * num_n;
+  const int per_xcd = (total + 7) / 8;
+  const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (L >= total) return;
+  const int mt = L % num_m, nt = L / num_m;
+  const int m0 = mt * BM;
+  const int nk = a.K / BK;
+
+  // thread -> 16-byte chunk mapping of the A and W tiles (rows of CPR chunks);
+  // recomputed where used rather than held in registers
+  const int c_row = tid / CPR, c_col = (tid % CPR) * 8;
+  constexpr int ROWS_PER_PASS = 256 / CPR;
+  const bf16_t* bp0 = b_ptr<EPI, BN, WN>(a, nt, c_row) + c_col;
+  // W rows of one pass are consecutive except where a segment or the gate/up
+  // pairing switches; those cases take the general pointer per chunk.
+  constexpr bool W_CONTIG = EPI == Epi::Store || EPI == Epi::AddTo || EPI == Epi::Argmax;
+  // Global loads run PD K steps ahead of the MFMAs.  With PD == 2, tile t
+  // waits in register set t & 1; the K loop is unrolled by two so every set
+  // index is a compile-time constant (no indexed register access).
+  u32x4 ra[PD][NA], rb[PD][NB];
+  auto fetch = [&](int kt, auto set_c) {
+    constexpr int set = decltype(set_c)::value;
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      if ((BM * CPR) % 256 == 0 || c_row + i * ROWS_PER_PASS < BM)
+        ra[set][i] = a_load<MODE>(a, min(m0 + c_row + i * ROWS_PER_PASS, a.M - 1), k0 + c_col);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int r = c_row + i * ROWS_PER_PASS;
+      if ((BN * CPR) % 256 != 0 && r >= BN) continue;
+      const bf16_t* p = W_CONTIG && b_row<EPI, BN, WN>(a, nt, r) < a.n_a
+                            ? bp0 + static_cast<int64_t>(i * ROWS_PER_PASS) * a.K
+                            : b_ptr<EPI, BN, WN>(a, nt, r) + c_col;
+      rb[set][i] = load16(p + k0);
+    }
+  };
+  auto stash = [&](auto buf_c, auto set_c) {
+    constexpr int buf = decltype(buf_c)::value, set = decltype(set_c)::value;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int r = c_row + i * ROWS_PER_PASS;
+      if ((BM * CPR) % 256 == 0 || r < BM) store16(&As[buf][lds_off<CPR>(r, c_col / 8)], ra[set][i]);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int r = c_row + i * ROWS_PER_PASS;
+      if ((BN * CPR) % 256 == 0 || r < BN) store16(&Bs[buf][lds_off<CPR>(r, c_col / 8)], rb[set][i]);
+    }
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using CS1 = std::integral_constant<int, PD == 2 ? 1 : 0>;
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int jn = 0; jn < TN; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int l16 = lane & 15, lq = lane >> 4;
+  auto compute = [&](auto buf_c) {
+    constexpr int cur = decltype(buf_c)::value;
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      // all W fragments of the K slice stay in registers; A fragments are
+      // read one at a time so the live set stays small
+      u32x4 bf[TN];
+#pragma unroll
+      for (int jn = 0; jn < TN; ++jn)
+        bf[jn] = *reinterpret_cast<const u32x4*>(&Bs[cur][lds_off<CPR>(wn * WN + jn * 16 + l16, ks * 4 + lq)]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const u32x4 af = *reinterpret_cast<const u32x4*>(&As[cur][lds_off<CPR>(wm * WM + i * 16 + l16, ks * 4 + lq)]);
+#pragma unroll
+        for (int jn = 0; jn < TN; ++jn)
+          acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af),
+                                                               __builtin_bit_cast(bf16x8, bf[jn]), acc[i][jn], 0, 0,
+                                                               0);
+      }
+    }
+  };
+  // one K step on LDS buffer B: compute, publish tile kt+1, request tile kt+1+PD
+  auto step = [&](int kt, auto buf_c) {
+    constexpr int cur = decltype(buf_c)::value;
+    using Nxt = std::integral_constant<int, cur ^ 1>;
+    // tile kt+1 lives in set (kt+1) % PD == (cur ^ 1) % PD, tile kt+1+PD reuses it
+    using SetN = std::integral_constant<int, PD == 2 ? (cur ^ 1) : 0>;
+    compute(buf_c);
+    if (kt + 1 < nk) stash(Nxt{}, SetN{});
+    if (kt + 1 + PD < nk) fetch(kt + 1 + PD, SetN{});
+    __syncthreads();
+  };
+
+  fetch(0, C0{});
+  if (PD == 2 && nk > 1) fetch(1, CS1{});
+  stash(C0{}, C0{});
+  if (PD == 1 && nk > 1) fetch(1, C0{});
+  if (PD == 2 && nk > 2) fetch(2, C0{});
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, C0{});
+    if (kt + 1 < nk) step(kt + 1, C1{});
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  static_assert(WGN * BM * sizeof(Top2) <= sizeof(Bs) / 2, "argmax scratch must fit one LDS buffer");
+  tile_epilogue<BM, BN, WGM, WGN, TM, TN, EPI>(a, acc, m0, nt, num_n, wm, wn, reinterpret_cast<Top2*>(&Bs[0][0]));
+}
+
+// Tile shapes (K step 32 for the 256-column tile, 64 for the others).
 struct TileCfg {
   int bm, bn;
 };
-constexpr TileCfg kLarge{256, 256}, kMedium{128, 128}, kSmall{128, 64};
+constexpr TileCfg kLarge{128, 256}, kMedium{128, 128}, kSmall{128, 64};
 
 int cols_per_tile(const TileCfg& t, Epi epi) { return epi == Epi::SiluMul ? t.bn / 2 : t.bn; }
 int tiles_of(const TileCfg& t, int M, int Nout, Epi epi) {
@@ -274,15 +338,16 @@ int tiles_of(const TileCfg& t, int M, int Nout, Epi epi) {
   return ((M + t.bm - 1) / t.bm) * ((Nout + c - 1) / c);
 }
 
-// Largest tile that still yields about one workgroup per CU (the 256-row tile
-// only when it is at least half used).
+// Largest tile that still fills the chip: the 256-column tile when there are
+// several M tiles to share each W tile in L2 and a workgroup per CU, the
+// 128-column tile with two workgroups per CU, else the 64-column tile.
 TileCfg pick_tile(int M, int Nout, Epi epi, int num_cus) {
   if (M > 128 && tiles_of(kLarge, M, Nout, epi) >= num_cus) return kLarge;
-  if (tiles_of(kMedium, M, Nout, epi) >= num_cus) return kMedium;
+  if (tiles_of(kMedium, M, Nout, epi) >= 2 * num_cus) return kMedium;
   return kSmall;
 }
 
-template <int BM, int BN, int BK, Epi EPI, AMode MODE>
+template <int BM, int BN, int BK, int PD, int WGM, Epi EPI, AMode MODE>
 hipError_t launch_t(GemvArgs& a, hipStream_t s) {
   const int num_m = (a.M + BM - 1) / BM;
   const int cols = EPI == Epi::SiluMul ? BN / 2 : BN;
@@ -290,16 +355,16 @@ hipError_t launch_t(GemvArgs& a, hipStream_t s) {
   const int total = num_m * num_n;
   const int grid = ((total + 7) / 8) * 8;
   a.grid_x = num_n;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, EPI, MODE>), dim3(grid), dim3(256), 0, s, a, num_m, num_n);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, PD, WGM, EPI, MODE>), dim3(grid), dim3(256), 0, s, a, num_m, num_n);
   return hipGetLastError();
 }
 
 template <Epi EPI, AMode MODE>
 hipError_t launch_cfg(GemvArgs& a, int num_cus, hipStream_t s) {
   const TileCfg t = pick_tile(a.M, a.Nout, EPI, num_cus);
-  if (t.bm == 256) return launch_t<256, 256, 32, EPI, MODE>(a, s);
-  if (t.bn == 128) return launch_t<128, 128, 64, EPI, MODE>(a, s);
-  return launch_t<128, 64, 64, EPI, MODE>(a, s);
+  if (t.bn == 256) return launch_t<128, 256, 32, 2, 2, EPI, MODE>(a, s);
+  if (t.bn == 128) return launch_t<128, 128, 64, 1, 2, EPI, MODE>(a, s);
+  return launch_t<128, 64, 64, 1, 2, EPI, MODE>(a, s);
 }
 
 }  // namespace
