@@ -13,10 +13,22 @@
 // softmax.  Each (row, head, split) leaves (acc[d], max, sum) in the workspace
 // and a second kernel merges the splits with their log-sum-exp weights and
 // stores the attention output as the next projection's operand.
+#include <type_traits>
+#include <utility>
+
 #include "common.h"
 
 namespace pe {
 namespace {
+
+template <typename F, size_t... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::index_sequence<I...>) {
+  (f(std::integral_constant<int, static_cast<int>(I)>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_index_sequence<N>{});
+}
 
 constexpr int QT = 64;  // queries per tile
 constexpr int KT = 64;  // keys per tile
@@ -144,28 +156,39 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
 // bf16, head_dim 64/128: the same split-KV attention on MFMA.
 //
 // A workgroup of 8 waves owns up to 128 queries (16 per wave) of one
-// (sequence, kv head, split).  Per 64-key tile the waves share K (row-major)
-// and V (transposed) in LDS.  Scores are formed transposed, S^T = K Q^T with
+// (sequence, kv head, split).  Per 64-key tile the waves share K and V in
+// LDS.  Scores are formed transposed, S^T = K Q^T with
 // v_mfma_f32_16x16x32_bf16 (keys are the A rows, the wave's queries the B
 // columns), so each lane owns one query column: the online-softmax row
 // statistics need only the 4 lanes that share that column, and the
 // probabilities are already in the B-operand layout of O^T += V^T P^T.  In
 // that product the MFMA's 32 k-slots of each 32-key half enumerate keys
 // 4j..4j+3 and 16+4j..16+4j+3 for lane group j, the order in which the score
-// tiles hold them.  K/V pieces of the next two tiles are kept in flight in
-// registers while the current tile is consumed from LDS.
-template <int D>
-__global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
+// tiles hold them.  K and V both stay row-major in
+// double-buffered LDS and the V^T operand of O^T += V^T P^T is formed by the
+// transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane i
+// receives element i % 4 of the 64-bit words read by lanes 4q + i / 4,
+// q = 0..3.  Lane 4q + c of group j therefore reads the four dims
+// 16 t + 4c .. 16 t + 4c + 3 of key 4j + q (and of key 16 + 4j + q for the
+// second word), which hands lane i of group j exactly the dim 16 t + i of
+// keys 4j..4j+3 and 16+4j..16+4j+3 -- the key order of the score tiles.  Rows
+// are padded by 32 bytes so the 16-row fragment reads and the transposing
+// reads spread over all banks.  One barrier per 64-key tile: tile t + 1 is
+// written to the other buffer while tile t is consumed.
+template <int D, int DEPTH, int OCC, bool LP>
+__global__ __launch_bounds__(512, OCC) void attn_mfma_kernel(AttnArgs a) {
   constexpr int KT = 64;
-  constexpr int KP = D + 8;    // padded K row (elements)
-  constexpr int VP = KT + 8;   // padded V^T row (elements)
+  constexpr int RP = D + 16;   // padded K / V row (elements)
   constexpr int DT = D / 16;   // O^T tiles
   constexpr int KK = D / 32;   // k-steps of S^T
   constexpr int PER = KT * D / 8 / 512;  // 16-byte K (and V) pieces per thread per tile
   static_assert(PER >= 1, "tile too small for the workgroup");
-  constexpr int MAXB = 1024;   // pages of one split held in LDS
-  __shared__ bf16_t ks[KT * KP];
-  __shared__ bf16_t vt[D * VP];
+  // LP: the split's page numbers sit in LDS (the host checked they fit), so
+  // K/V addresses do not wait on a block-table load
+  constexpr int MAXB = LP ? kAttnMaxPages : 1;
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(16))) bf16_t ks[2][KT * RP];
+  __shared__ __attribute__((aligned(16))) bf16_t vs[2][KT * RP];
   __shared__ int32_t pages[MAXB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, j = lane >> 4;
   const int sp = blockIdx.x, g = blockIdx.y, i = blockIdx.z;
@@ -183,43 +206,43 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
   const bf16_t* vc = static_cast<const bf16_t*>(a.v_cache);
   const int32_t* bt = a.block_table + static_cast<int64_t>(i) * a.max_blocks;
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  // the split's page numbers, so K/V addresses do not wait on a table load
-  const int pg0 = kb / a.block_size;
-  const int npg = ke > kb ? (ke - 1) / a.block_size - pg0 + 1 : 0;
-  const bool paged_lds = npg <= MAXB;
-  for (int q = tid; q < npg && paged_lds; q += 512) pages[q] = bt[pg0 + q];
+  constexpr int BS = 16;  // KV page size (the only one the library accepts)
+  const int pg0 = kb / BS;
+  const int npg = ke > kb ? (ke - 1) / BS - pg0 + 1 : 0;
+  if (LP)
+    for (int q = tid; q < min(npg, MAXB); q += 512) pages[q] = bt[pg0 + q];
   __syncthreads();
 
-  constexpr int DEPTH = 3;  // tiles in flight
+  // DEPTH tiles in flight in registers beyond the one in LDS; tile u waits in
+  // register set u % DEPTH and is consumed from LDS buffer u % 2
+  static_assert(DEPTH >= 2 && DEPTH <= 4, "2..4 tiles in flight");
+  constexpr int U = DEPTH % 2 == 0 ? DEPTH : 2 * DEPTH;
   u32x4 kr[DEPTH][PER], vr[DEPTH][PER];
-  auto fetch = [&](int t, int set) {
+  // Requests are unconditional (positions past the split's end are clamped to
+  // its last key, whose values are finite and whose probability is zero), so
+  // every lane issues the same loads and the compiler's counters of
+  // outstanding loads stay exact: staging tile t + 1 waits only for it.
+  auto fetch = [&](int t, auto set_c) {
+    constexpr int set = decltype(set_c)::value;
 #pragma unroll
     for (int pp = 0; pp < PER; ++pp) {
       const int piece = tid + 512 * pp;
       const int key = piece / (D / 8), c8 = piece % (D / 8);
-      const int p = kb + t * KT + key;
-      kr[set][pp] = zero;
-      vr[set][pp] = zero;
-      if (p < ke) {
-        const int64_t blk = paged_lds ? pages[p / a.block_size - pg0] : bt[p / a.block_size];
-        const int64_t off = ((blk * a.n_kv + g) * a.block_size + p % a.block_size) * D + c8 * 8;
-        kr[set][pp] = load16(kc + off);
-        vr[set][pp] = load16(vc + off);
-      }
+      const int p = min(kb + t * KT + key, ke - 1);
+      const int64_t blk = LP ? pages[p / BS - pg0] : bt[p / BS];
+      const int64_t off = ((blk * a.n_kv + g) * BS + p % BS) * D + c8 * 8;
+      kr[set][pp] = load16(kc + off);
+      vr[set][pp] = load16(vc + off);
     }
   };
-  auto stash = [&](int set) {
+  auto stash = [&](auto buf_c, auto set_c) {
+    constexpr int buf = decltype(buf_c)::value, set = decltype(set_c)::value;
 #pragma unroll
     for (int pp = 0; pp < PER; ++pp) {
       const int piece = tid + 512 * pp;
       const int key = piece / (D / 8), c8 = piece % (D / 8);
-      store16(ks + key * KP + c8 * 8, kr[set][pp]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t w = vr[set][pp][e];
-        vt[(c8 * 8 + 2 * e) * VP + key] = static_cast<bf16_t>(w & 0xffffu);
-        vt[(c8 * 8 + 2 * e + 1) * VP + key] = static_cast<bf16_t>(w >> 16);
-      }
+      store16(&ks[buf][key * RP + c8 * 8], kr[set][pp]);
+      store16(&vs[buf][key * RP + c8 * 8], vr[set][pp]);
     }
   };
 
@@ -229,6 +252,10 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
     const int h = g * grp + qn % grp;
     const bool active = qn < nqry && !a.rejected[row];
     const int qpos = active ? a.pos[row] : -1;
+    // smallest causal bound among this wave's active queries
+    int wave_qmin = active ? qpos : 0x7fffffff;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) wave_qmin = min(wave_qmin, __shfl_xor(wave_qmin, off, 64));
     u32x4 qf[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
@@ -238,70 +265,112 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int t = 0; t < DT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-    for (int t = 0; t < DEPTH; ++t)
-      if (t < ntiles) fetch(t, t);
-    for (int t = 0; t < ntiles; ++t) {
+    auto compute = [&](int t, auto buf_c) {
+      constexpr int buf = decltype(buf_c)::value;
       const int kt0 = kb + t * KT;
-      const int set = t % DEPTH;
-      __syncthreads();
-      stash(set);
-      __syncthreads();
-      if (t + DEPTH < ntiles) fetch(t + DEPTH, set);
-
       f32x4 st[4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int mt = 0; mt < 4; ++mt) st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // d-slices outer, key tiles inner: consecutive MFMAs are independent
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const u32x4 af = *reinterpret_cast<const u32x4*>(ks + (mt * 16 + (lane & 15)) * KP + 32 * kk + 8 * j);
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const u32x4 af =
+              *reinterpret_cast<const u32x4*>(&ks[buf][(mt * 16 + (lane & 15)) * RP + 32 * kk + 8 * j]);
           st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af),
                                                            __builtin_bit_cast(bf16x8, qf[kk]), st[mt], 0, 0, 0);
         }
-      }
+      // online softmax in base 2 with the 1/sqrt(d) scale folded into one FMA:
+      // p = 2^(s * sl2 - m), m the running maximum of s * sl2.  A tile that
+      // lies wholly inside every query's causal range of this wave (the common
+      // case) skips the per-key masks.
+      const bool full = kt0 + KT <= ke && kt0 + KT - 1 <= wave_qmin;
       float sv[16];
       float mx = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int p = kt0 + mt * 16 + 4 * j + q;
-          const float sc = (p < ke && p <= qpos) ? st[mt][q] * sl2 : -INFINITY;
-          sv[mt * 4 + q] = sc;
-          mx = fmaxf(mx, sc);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float corr = m_run == -INFINITY ? (m_new == -INFINITY ? 1.f : 0.f) : exp2f(m_run - m_new);
+          for (int q = 0; q < 4; ++q) {
+            sv[mt * 4 + q] = st[mt][q];
+            mx = fmaxf(mx, st[mt][q]);
+          }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int p = kt0 + mt * 16 + 4 * j + q;
+            const float sc = (p < ke && p <= qpos) ? st[mt][q] : -INFINITY;
+            sv[mt * 4 + q] = sc;
+            mx = fmaxf(mx, sc);
+          }
+      }
+      mx = xor32_max(xor16_max(mx));
+      const float m_new = fmaxf(m_run, mx * sl2);
+      // all keys so far masked: keep the sums at zero (m_new = -inf)
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
       float rs = 0.f;
       uint32_t pk[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p0 = sv[2 * e] == -INFINITY ? 0.f : exp2f(sv[2 * e] - m_new);
-        const float p1 = sv[2 * e + 1] == -INFINITY ? 0.f : exp2f(sv[2 * e + 1] - m_new);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[2 * e], sl2, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[2 * e + 1], sl2, -m_use));
         rs += p0 + p1;
-        pk[e] = static_cast<uint32_t>(f32_to_bf16(p0)) | (static_cast<uint32_t>(f32_to_bf16(p1)) << 16);
+        pk[e] = pack_bf16x2(p0, p1);
       }
-      rs += __shfl_xor(rs, 16, 64);
-      rs += __shfl_xor(rs, 32, 64);
+      rs = xor32_sum(xor16_sum(rs));
       l_run = l_run * corr + rs;
       m_run = m_new;
+      // transposing-read address of this lane: key 4j + (lane % 16) / 4, dims
+      // 4 (lane % 4) .. + 3 of each 16-dim tile
+      const bf16_t* vb = &vs[buf][(4 * j + ((lane & 15) >> 2)) * RP + 4 * (lane & 3)];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const u32x4 pb = {pk[4 * hf], pk[4 * hf + 1], pk[4 * hf + 2], pk[4 * hf + 3]};
 #pragma unroll
         for (int t2 = 0; t2 < DT; ++t2) {
           if (hf == 0) o[t2] *= corr;
-          const bf16_t* vr_ = vt + (t2 * 16 + (lane & 15)) * VP + hf * 32;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vr_ + 4 * j);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vr_ + 16 + 4 * j);
-          const u32x4 af = {lo.x, lo.y, hi.x, hi.y};
+          const bf16_t* src = vb + (hf * 32) * RP + t2 * 16;
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)(src));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)(src + 16 * RP));
+          const u32x4 af = {__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                            __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y};
           o[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af),
                                                           __builtin_bit_cast(bf16x8, pb), o[t2], 0, 0, 0);
         }
       }
+    };
+
+    // prologue: tiles 0 .. DEPTH - 1 requested, tile 0 published in buffer 0,
+    // tile DEPTH requested into the freed register set
+    if (ntiles > 0) {
+      static_for<DEPTH>([&](auto s_c) { fetch(min(static_cast<int>(decltype(s_c)::value), ntiles - 1), s_c); });
+      using Z = std::integral_constant<int, 0>;
+      stash(Z{}, Z{});
+      fetch(min(DEPTH, ntiles - 1), Z{});
+    }
+    __syncthreads();
+    // tile t: consume its buffer, publish tile t + 1 in the other buffer,
+    // request tile t + 1 + DEPTH into the register set tile t + 1 freed
+    for (int t0 = 0; t0 < ntiles; t0 += U) {
+      static_for<U>([&](auto j_c) {
+        constexpr int jj = decltype(j_c)::value;
+        const int t = t0 + jj;
+        if (t < ntiles) {
+          compute(t, std::integral_constant<int, jj & 1>{});
+          using Nb = std::integral_constant<int, (jj + 1) & 1>;
+          using Ns = std::integral_constant<int, (jj + 1) % DEPTH>;
+          // past the last tile these publish / request clamped, unused data
+          stash(Nb{}, Ns{});
+          fetch(min(t + 1 + DEPTH, ntiles - 1), Ns{});
+          __syncthreads();
+        }
+      });
     }
     if (qn < nqry && !a.rejected[row]) {
       float* out = a.partial + ((static_cast<int64_t>(row) * a.n_q + h) * a.splits + sp) * (D + 2);
@@ -346,14 +415,25 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
   }
 }
 
+template <int D>
+void launch_mfma(const AttnArgs& a, dim3 grid, hipStream_t s) {
+  // 64-dim heads: two workgroups per CU; 128-dim heads: one, with a deeper
+  // register prefetch (two would spill)
+  constexpr int DEPTH = D == 64 ? 2 : 3, OCC = D == 64 ? 4 : 2;
+  if (a.max_blocks <= (kAttnMaxPages - 8) * a.splits)
+    hipLaunchKernelGGL((attn_mfma_kernel<D, DEPTH, OCC, true>), grid, dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<D, DEPTH, OCC, false>), grid, dim3(512), 0, s, a);
+}
+
 template <typename T>
 hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.splits, a.n_kv, a.c);
   if (sizeof(T) == 2 && (a.d == 64 || a.d == 128)) {
     if (a.d == 64)
-      hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, dim3(512), 0, s, a);
+      launch_mfma<64>(a, grid, s);
     else
-      hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, dim3(512), 0, s, a);
+      launch_mfma<128>(a, grid, s);
   } else {
     switch (a.d) {
       case 16: hipLaunchKernelGGL((attn_split_kernel<T, 16>), grid, dim3(256), 0, s, a); break;
