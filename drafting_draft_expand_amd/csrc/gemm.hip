@@ -71,17 +71,6 @@ __device__ __forceinline__ int lds_off(int r, int c) {
   return r * (CPR * 8) + sw * 8;
 }
 
-template <AMode MODE>
-__device__ __forceinline__ u32x4 a_load(const GemvArgs& a, int m, int k) {
-  if constexpr (MODE == AMode::Gather) {
-    const int half = a.K / 2;
-    if (k < half) return load16(static_cast<const bf16_t*>(a.embed) + static_cast<int64_t>(a.ids[m]) * half + k);
-    return load16(static_cast<const bf16_t*>(a.x2) + static_cast<int64_t>(m) * half + (k - half));
-  } else {
-    return load16(static_cast<const bf16_t*>(a.x) + static_cast<int64_t>(m) * a.K + k);
-  }
-}
-
 // Epilogue of one output tile held in MFMA accumulators: wave (wm, wn) of a
 // WGM x WGN wave grid owns rows m0 + wm * 16 TM .. and tile columns
 // wn * 16 TN ..; lane l holds rows 4 (l / 16) + q, column l % 16 of each
@@ -236,13 +225,31 @@ __global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel
   // waits in register set t & 1; the K loop is unrolled by two so every set
   // index is a compile-time constant (no indexed register access).
   u32x4 ra[PD][NA], rb[PD][NB];
+  // A source rows, resolved once (for the gathered operand: the token's
+  // embedding row and the row's draft hidden state, each K/2 wide)
+  const bf16_t* ap0[NA];
+  const bf16_t* ap1[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int m = min(m0 + c_row + i * ROWS_PER_PASS, a.M - 1);
+    if constexpr (MODE == AMode::Gather) {
+      const int half = a.K / 2;
+      ap0[i] = static_cast<const bf16_t*>(a.embed) + static_cast<int64_t>(a.ids[m]) * half + c_col;
+      ap1[i] = static_cast<const bf16_t*>(a.x2) + static_cast<int64_t>(m) * half + c_col - half;
+    } else {
+      ap0[i] = static_cast<const bf16_t*>(a.x) + static_cast<int64_t>(m) * a.K + c_col;
+      ap1[i] = ap0[i];
+    }
+  }
   auto fetch = [&](int kt, auto set_c) {
     constexpr int set = decltype(set_c)::value;
     const int k0 = kt * BK;
 #pragma unroll
     for (int i = 0; i < NA; ++i)
-      if ((BM * CPR) % 256 == 0 || c_row + i * ROWS_PER_PASS < BM)
-        ra[set][i] = a_load<MODE>(a, min(m0 + c_row + i * ROWS_PER_PASS, a.M - 1), k0 + c_col);
+      if ((BM * CPR) % 256 == 0 || c_row + i * ROWS_PER_PASS < BM) {
+        const bool lo = MODE != AMode::Gather || k0 + c_col < a.K / 2;
+        ra[set][i] = load16((lo ? ap0[i] : ap1[i]) + k0);
+      }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int r = c_row + i * ROWS_PER_PASS;
