@@ -13,22 +13,10 @@
 // softmax.  Each (row, head, split) leaves (acc[d], max, sum) in the workspace
 // and a second kernel merges the splits with their log-sum-exp weights and
 // stores the attention output as the next projection's operand.
-#include <type_traits>
-#include <utility>
-
 #include "common.h"
 
 namespace pe {
 namespace {
-
-template <typename F, size_t... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::index_sequence<I...>) {
-  (f(std::integral_constant<int, static_cast<int>(I)>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_index_sequence<N>{});
-}
 
 constexpr int QT = 64;  // queries per tile
 constexpr int KT = 64;  // keys per tile

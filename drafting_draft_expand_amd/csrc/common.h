@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "internal.h"
 
 namespace pe {
@@ -12,6 +15,17 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled: register
+// arrays indexed by i stay in registers.
+template <typename F, size_t... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::index_sequence<I...>) {
+  (f(std::integral_constant<int, static_cast<int>(I)>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_index_sequence<N>{});
+}
 
 // bfloat16 is carried as raw uint16 bit patterns.
 typedef uint16_t bf16_t;

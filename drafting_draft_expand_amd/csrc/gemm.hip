@@ -115,38 +115,42 @@ __device__ __forceinline__ void tile_epilogue(const GemvArgs& a, f32x4 (&acc)[TM
   } else if constexpr (EPI == Epi::QkvRope) {
     const RopeOut& ro = a.rope;
     const int d = ro.d;
+    // row metadata once per row (rows outer), columns inner
 #pragma unroll
-    for (int jn = 0; jn < TN; ++jn) {
-      const int col = nt * BN + wn * WN + jn * 16 + l16;
-      const int n = b_row<EPI, BN, WN>(a, nt, wn * WN + jn * 16 + l16);
-      const int head = n / d;
-      const int e = n - head * d;
-      const bool rotate = head < ro.n_q + ro.n_kv;
-      const double inv_freq = ro.freq.inv[e % (d / 2)];
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int q = 0; q < 4; ++q) {
+        const int m = m0 + wm * WM + i * 16 + lq * 4 + q;
+        const int mc = min(m, a.M - 1);
+        const bool live = m < a.M && !ro.rejected[mc];
+        const int pos = ro.pos[mc];
+        const int64_t slot = ro.slot[mc];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int m = m0 + wm * WM + i * 16 + lq * 4 + q;
+        for (int jn = 0; jn < TN; ++jn) {
+          const int col = nt * BN + wn * WN + jn * 16 + l16;
+          const int n = b_row<EPI, BN, WN>(a, nt, wn * WN + jn * 16 + l16);
+          const int head = n / d;
+          const int e = n - head * d;
+          const bool rotate = head < ro.n_q + ro.n_kv;
           const float v = acc[i][jn][q];
           const float partner = __shfl_xor(v, 8, 64);
-          if (m >= a.M || col >= a.Nout || ro.rejected[m]) continue;
+          if (!live || col >= a.Nout) continue;
           float out = v;
           if (rotate) {
             float cs, sn;
-            rope_cos_sin(ro.pos[m], inv_freq, cs, sn);
+            rope_cos_sin(pos, ro.freq.inv[e % (d / 2)], cs, sn);
             out = (l16 & 8) == 0 ? v * cs - partner * sn : v * cs + partner * sn;
           }
           if (head < ro.n_q) {
             static_cast<bf16_t*>(ro.q_out)[(static_cast<int64_t>(m) * ro.n_q + head) * d + e] = f32_to_bf16(out);
           } else {
-            const int64_t slot = ro.slot[m];
             if (slot < 0) continue;
             const bool is_k = head < ro.n_q + ro.n_kv;
             const int g = is_k ? head - ro.n_q : head - ro.n_q - ro.n_kv;
-            const int64_t blk = slot / ro.block_size;
-            const int off = static_cast<int>(slot - blk * ro.block_size);
-            static_cast<bf16_t*>(is_k ? ro.k_cache : ro.v_cache)[((blk * ro.n_kv + g) * ro.block_size + off) * d + e] =
+            // 16-token pages (the only page size the library accepts)
+            const int64_t blk = slot >> 4;
+            const int off = static_cast<int>(slot & 15);
+            static_cast<bf16_t*>(is_k ? ro.k_cache : ro.v_cache)[((blk * ro.n_kv + g) * 16 + off) * d + e] =
                 f32_to_bf16(out);
           }
         }

@@ -246,6 +246,23 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
   }
   const float inv = (MODE == AMode::Norm && xvalid) ? inv_s[lane & 15] : 0.f;
   const int T = (a.Nout + 15) / 16;
+  // q/k/v epilogue: the position, rejected flag and cache slot of this lane's
+  // four output rows are read once, before the weights stream, instead of
+  // after the K loop on every tile (they would be serialised behind the stores)
+  int r_pos[4] = {0, 0, 0, 0};
+  int64_t r_slot[4] = {-1, -1, -1, -1};
+  bool r_live[4] = {false, false, false, false};
+  if constexpr (EPI == Epi::QkvRope) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int m = m0 + 4 * j + q;
+      if (m < a.M) {
+        r_live[q] = !a.rope.rejected[m];
+        r_pos[q] = a.rope.pos[m];
+        r_slot[q] = a.rope.slot[m];
+      }
+    }
+  }
   const u32x4 zero = {0u, 0u, 0u, 0u};
   Top2 best[4];
 #pragma unroll
@@ -358,23 +375,24 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
           const int m = m0 + 4 * j + q;
           const float v = sum[0][q];
           const float partner = __shfl_xor(v, 8, 64);
-          if (m >= a.M || ro.rejected[m]) continue;
+          if (!r_live[q]) continue;
           float out = v;
           if (rotate) {
             float cs, sn;
-            rope_cos_sin(ro.pos[m], inv_freq, cs, sn);
+            rope_cos_sin(r_pos[q], inv_freq, cs, sn);
             out = c < 8 ? v * cs - partner * sn : v * cs + partner * sn;
           }
           if (head < ro.n_q) {
             static_cast<bf16_t*>(ro.q_out)[(static_cast<int64_t>(m) * ro.n_q + head) * d + e] = f32_to_bf16(out);
           } else {
-            const int64_t slot = ro.slot[m];
+            const int64_t slot = r_slot[q];
             if (slot < 0) continue;
             const bool is_k = head < ro.n_q + ro.n_kv;
             const int g = is_k ? head - ro.n_q : head - ro.n_q - ro.n_kv;
-            const int64_t blk = slot / ro.block_size;
-            const int off = static_cast<int>(slot - blk * ro.block_size);
-            static_cast<bf16_t*>(is_k ? ro.k_cache : ro.v_cache)[((blk * ro.n_kv + g) * ro.block_size + off) * d + e] =
+            // 16-token pages (the only page size the library accepts)
+            const int64_t blk = slot >> 4;
+            const int off = static_cast<int>(slot & 15);
+            static_cast<bf16_t*>(is_k ? ro.k_cache : ro.v_cache)[((blk * ro.n_kv + g) * 16 + off) * d + e] =
                 f32_to_bf16(out);
           }
         }

@@ -177,6 +177,26 @@ def test_forward_qwen_c16_sampled(K):
     _forward_case(wl, seqs=pick, batch=b)
 
 
+@pytest.mark.parametrize("name", ["gptoss20b-bf16-c1-k7", "small-bf16-c2", "gptoss20b-bf16-c64-k7"])
+def test_forward_without_logits_matches(name):
+    """The token-only pass (what the bench times) picks the same tokens and
+    top-2 gaps as the pass that also writes the logits."""
+    if name == "small-bf16-c2":
+        spec = synth.ModelSpec(hidden=256, vocab=1000, n_layers=1, n_q=8, n_kv=2, head_dim=64, inter=512)
+        wl = synth.Workload(name, spec, c=2, K=7, ctx_lo=10, ctx_hi=300, accept_hi=7, seed=44)
+    else:
+        wl = synth.WORKLOADS[name]
+    _say(f"no-logits path {wl.name}")
+    model = device_model(wl.model, wl.wseed)
+    b = synth.make_batch(wl)
+    db = upload_batch(b, "cuda:0")
+    _, tok_a, _, gap_a = gpu_round(model, db, b.K, want_logits=True)
+    tok_a, gap_a = from_torch(tok_a).copy(), from_torch(gap_a).copy()
+    _, tok_b, _, gap_b = gpu_round(model, db, b.K, want_logits=False)
+    assert np.array_equal(tok_a, from_torch(tok_b))
+    assert np.array_equal(gap_a, from_torch(gap_b))
+
+
 # ----------------------------------------------------------------------------- acceptance
 @pytest.mark.parametrize("name", ["tiny-fp32-c2-k3", "qwen3coder30b-bf16-c16-k7"])
 def test_accept_matches_oracle(name):
