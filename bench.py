@@ -64,7 +64,7 @@ def step_bytes(spec, wl, b) -> int:
     return (w + kv_read) * eb + hid + emb
 
 
-def _cpu_baseline(wl, w, b, budget_s: float):
+def _cpu_baseline(wl, w, b, budget_s: float, mode: str = "peagle"):
     import numpy as np
     import oracle
     try:
@@ -76,10 +76,12 @@ def _cpu_baseline(wl, w, b, budget_s: float):
     rounds = 0
     t0 = time.perf_counter()
     while True:
-        r = oracle.parallel_draft_step(wl.model, w, b, want_logits=False)
-        tgt = __import__("synth").target_tokens_from_drafts(r["forward"]["tokens"], u, alt, wl.agree_probs(),
-                                                              wl.model.vocab)
-        oracle.accept(r["forward"]["tokens"], tgt)
+        if mode == "ar":
+            drafts = oracle.autoregressive_draft(wl.model, w, b, wl.K)["tokens"]
+        else:
+            drafts = oracle.parallel_draft_step(wl.model, w, b, want_logits=False)["forward"]["tokens"]
+        tgt = __import__("synth").target_tokens_from_drafts(drafts, u, alt, wl.agree_probs(), wl.model.vocab)
+        oracle.accept(drafts, tgt)
         rounds += 1
         el = time.perf_counter() - t0
         if el >= budget_s or rounds >= 20:
@@ -88,7 +90,8 @@ def _cpu_baseline(wl, w, b, budget_s: float):
     return dict(value=round(rounds * wl.c * wl.K / el, 3), unit="draft tokens/s", cores=int(threads),
                 kind="oracle",
                 sample=f"{rounds} full round(s) of {wl.name} through the float64 oracle "
-                       f"(expand, placement, drafter pass, argmax, acceptance), {el:.1f} s")
+                       + ("(K one-token drafter passes, argmax, acceptance)" if mode == "ar" else
+                          "(expand, placement, drafter pass, argmax, acceptance)") + f", {el:.1f} s")
 
 
 def _calibrate_copy() -> int:
@@ -114,6 +117,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--eager", action="store_true", help="time eager launches only (no HIP graph replay)")
+    ap.add_argument("--mode", choices=("peagle", "ar", "loop"), default="peagle",
+                    help="peagle: one parallel-draft round per step; ar: the K-pass autoregressive baseline "
+                         "on the same kernels; loop: rounds chained through the device-built next batch")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy five times (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -134,7 +140,9 @@ def main() -> int:
     dev = "cuda:0"
     t_setup = time.perf_counter()
     w = synth.make_weights(spec, wl.wseed)
-    b = synth.make_batch(wl)
+    # the chained loop advances every sequence by up to K+1 positions a round
+    b = synth.make_batch(wl, extra_positions=(args.steps + args.warmup + 2) * (wl.K + 1) if args.mode == "loop"
+                         else 0)
     dw = upload_weights(w, dev)
     db = upload_batch(b, dev)
     model = pe.DraftModel.from_spec(spec, dw)
@@ -159,6 +167,33 @@ def main() -> int:
                          tokens=tokens, stream=stream)
         pe.accept(tokens, tgt, acc, bonus, stream=stream)
 
+    if args.mode == "ar":
+        ar_ws = torch.empty(model.autoregressive_workspace_bytes(c, K, T), dtype=torch.uint8, device=dev)
+
+        def step():  # noqa: F811 -- K one-token passes instead of one parallel pass
+            pe.draft_autoregressive(model, K, db["query_lens"], db["target_ids"], db["target_pos"],
+                                    db["num_accepted"], db["bonus_ids"], db["target_hidden"], db["block_table"],
+                                    db["k_cache"], db["v_cache"], workspace=ar_ws, tokens=tokens, stream=stream)
+            pe.accept(tokens, tgt, acc, bonus, stream=stream)
+    elif args.mode == "loop":
+        # rounds chained on the device: accept's outputs and the next verified
+        # batch feed the next prepare; the verifier's tokens and hidden states
+        # are fixed synthetic buffers (the target model is not part of the path)
+        cur = {k: db[k] for k in ("query_lens", "target_ids", "target_pos", "num_accepted", "bonus_ids")}
+        nxt = pe.next_verified_batch(K, prep["kv_lens"], cur["bonus_ids"], tokens, acc, bonus)
+        hid_next = db["target_hidden"]
+
+        def step():  # noqa: F811
+            pe.prepare_draft_batch(model, K, cur["query_lens"], cur["target_ids"], cur["target_pos"],
+                                   cur["num_accepted"], cur["bonus_ids"], hid_next, db["block_table"], out=prep,
+                                   stream=stream)
+            pe.draft_forward(model, prep, db["block_table"], db["k_cache"], db["v_cache"], workspace=ws,
+                             tokens=tokens, stream=stream)
+            pe.accept(tokens, tgt, acc, bonus, stream=stream)
+            pe.next_verified_batch(K, prep["kv_lens"], cur["bonus_ids"], tokens, acc, bonus, out=nxt, stream=stream)
+            for k in cur:
+                cur[k].copy_(nxt[k])
+
     def timed(fn, n):
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -179,7 +214,7 @@ def main() -> int:
     model.timing_enable(pe.PE_KERNEL_LM_HEAD, False)
     ms_per_step, mode = eager_ms, "eager"
     graph_ms = None
-    if not args.eager:
+    if not args.eager and args.mode == "peagle":
         # the same round captured once into a HIP graph and replayed (the
         # deployment form: fixed shapes, one submission per round)
         graph = torch.cuda.CUDAGraph()
@@ -215,7 +250,7 @@ def main() -> int:
         rec = tf.get(wl.name)
         if rec and rec.get("src_hash") == _src_hash(rec.get("sources", [])):
             traffic = rec.get("bytes_per_launch")
-    sb = step_bytes(spec, wl, b)
+    sb = step_bytes(spec, wl, b) * (K if args.mode == "ar" else 1)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -225,6 +260,7 @@ def main() -> int:
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "launch_mode": mode,
+        "mode": args.mode,
         "eager_ms_per_step": round(eager_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -245,7 +281,7 @@ def main() -> int:
                           "unit": "GB/s", "frac": round(sb / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = _cpu_baseline(wl, w, b, args.cpu_budget)
+        out["cpu_baseline"] = _cpu_baseline(wl, w, b, args.cpu_budget, args.mode)
     model.close()
     print(json.dumps(out), flush=True)
     return 0

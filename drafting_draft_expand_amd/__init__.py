@@ -6,14 +6,18 @@ Public API (thin ctypes binding over libpeagle.so; all work runs in HIP):
 * :func:`prepare_draft_batch` -- expand the verified batch, place hidden states
 * :func:`draft_forward` -- one drafter pass producing K tokens per sequence
 * :func:`accept` -- greedy accepted length and next bonus token
+* :func:`draft_autoregressive` -- the K-pass autoregressive baseline on the same kernels
+* :func:`next_verified_batch` -- next round's verified batch from this round's results
 """
 
 from ._lib import (  # noqa: F401
     DraftModel,
     PeError,
     accept,
+    draft_autoregressive,
     draft_forward,
     load,
+    next_verified_batch,
     prepare_draft_batch,
     status_string,
     PE_KERNEL_LM_HEAD,

@@ -22,7 +22,8 @@ PE_F32, PE_BF16 = 0, 1
 PE_KERNEL_LM_HEAD, PE_KERNEL_PREPARE, PE_KERNEL_ATTENTION = 0, 1, 2
 
 EXPORTED = ("pe_model_create", "pe_model_destroy", "pe_workspace_bytes", "pe_prepare_draft_batch",
-            "pe_draft_forward", "pe_accept", "pe_status_string", "pe_timing_enable", "pe_timing_read")
+            "pe_draft_forward", "pe_accept", "pe_status_string", "pe_timing_enable", "pe_timing_read",
+            "pe_autoregressive_workspace_bytes", "pe_draft_autoregressive", "pe_next_verified_batch")
 
 
 class PeError(RuntimeError):
@@ -79,6 +80,12 @@ def load() -> ctypes.CDLL:
     lib.pe_timing_enable.restype = I32
     lib.pe_timing_read.argtypes = [P, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]
     lib.pe_timing_read.restype = I32
+    lib.pe_autoregressive_workspace_bytes.argtypes = [P, I32, I32, I32]
+    lib.pe_autoregressive_workspace_bytes.restype = SZ
+    lib.pe_draft_autoregressive.argtypes = [P, I32, I32, I32] + [P] * 7 + [I32] + [P, P, P, SZ, P, P]
+    lib.pe_draft_autoregressive.restype = I32
+    lib.pe_next_verified_batch.argtypes = [I32, I32] + [P] * 10 + [P]
+    lib.pe_next_verified_batch.restype = I32
     _lib = lib
     return lib
 
@@ -142,6 +149,9 @@ class DraftModel:
 
     def workspace_bytes(self, num_seqs: int, K: int, num_rows: int) -> int:
         return int(load().pe_workspace_bytes(self.handle, num_seqs, K, num_rows))
+
+    def autoregressive_workspace_bytes(self, num_seqs: int, K: int, total_target_rows: int) -> int:
+        return int(load().pe_autoregressive_workspace_bytes(self.handle, num_seqs, K, total_target_rows))
 
     def timing_enable(self, kernel: int, enable: bool = True) -> None:
         _check(load().pe_timing_enable(self.handle, kernel, int(enable)), "pe_timing_enable")
@@ -229,3 +239,46 @@ def accept(draft_tokens: torch.Tensor, target_tokens: torch.Tensor, num_accepted
                           _stream(stream))
     _check(st, "pe_accept")
     return num_accepted, bonus_ids
+
+
+def draft_autoregressive(model: DraftModel, K: int, query_lens: torch.Tensor, target_ids: torch.Tensor,
+                         target_pos: torch.Tensor, num_accepted: torch.Tensor, bonus_ids: torch.Tensor,
+                         target_hidden: torch.Tensor, block_table: torch.Tensor, k_cache: Sequence[torch.Tensor],
+                         v_cache: Sequence[torch.Tensor], workspace: Optional[torch.Tensor] = None,
+                         tokens: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """K sequential one-token drafter passes (see pe_draft_autoregressive).  Returns tokens [c, K] (int32)."""
+    c = int(query_lens.numel())
+    T = int(target_ids.numel())
+    dev = target_ids.device
+    if workspace is None:
+        workspace = torch.empty(model.autoregressive_workspace_bytes(c, K, T), dtype=torch.uint8, device=dev)
+    if tokens is None:
+        tokens = torch.empty((c, K), dtype=torch.int32, device=dev)
+    kp = (ctypes.c_void_p * len(k_cache))(*[_ptr(t) for t in k_cache])
+    vp = (ctypes.c_void_p * len(v_cache))(*[_ptr(t) for t in v_cache])
+    st = load().pe_draft_autoregressive(
+        model.handle, c, K, T, _ptr(query_lens), _ptr(target_ids), _ptr(target_pos), _ptr(num_accepted),
+        _ptr(bonus_ids), _ptr(target_hidden), _ptr(block_table), int(block_table.shape[1]),
+        ctypes.cast(kp, ctypes.c_void_p), ctypes.cast(vp, ctypes.c_void_p), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(tokens), _stream(stream))
+    _check(st, "pe_draft_autoregressive")
+    return tokens
+
+
+def next_verified_batch(K: int, kv_lens: torch.Tensor, bonus_ids: torch.Tensor, draft_tokens: torch.Tensor,
+                        num_accepted_next: torch.Tensor, bonus_next: torch.Tensor,
+                        out: Optional[Dict[str, torch.Tensor]] = None, stream=None) -> Dict[str, torch.Tensor]:
+    """Next round's verified batch metadata (see pe_next_verified_batch)."""
+    c = int(kv_lens.numel())
+    dev = kv_lens.device
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = dict(query_lens=torch.empty(c, **i32), target_ids=torch.empty(c * (K + 1), **i32),
+                   target_pos=torch.empty(c * (K + 1), **i32), num_accepted=torch.empty(c, **i32),
+                   bonus_ids=torch.empty(c, **i32))
+    st = load().pe_next_verified_batch(
+        c, K, _ptr(kv_lens), _ptr(bonus_ids), _ptr(draft_tokens), _ptr(num_accepted_next), _ptr(bonus_next),
+        _ptr(out["query_lens"]), _ptr(out["target_ids"]), _ptr(out["target_pos"]), _ptr(out["num_accepted"]),
+        _ptr(out["bonus_ids"]), _stream(stream))
+    _check(st, "pe_next_verified_batch")
+    return out

@@ -440,6 +440,124 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
   return PE_OK;
 }
 
+// ---------------------------------------------------------------- autoregressive baseline
+namespace {
+// Workspace of the autoregressive baseline: the one-token first pass over the
+// T verified rows, the single-row passes, the drafter workspace they share.
+struct ArWorkspace {
+  size_t meta1, hid1, metak, hidk, tok, fwd, total;
+  size_t fwd_bytes;
+};
+ArWorkspace plan_ar(const pe_model* m, int c, int T) {
+  const size_t eb = m->d.dtype == PE_F32 ? 4 : 2;
+  const size_t H = m->d.hidden;
+  auto meta_bytes = [&](size_t rows) {
+    // ids, pos (i32), slot (i64), rejected, masked (u8), hidden map (i32), cu (c+1), kv lens, sample idx
+    return align_up(rows * 4) * 2 + align_up(rows * 8) + align_up(rows) * 2 + align_up(rows * 4) +
+           align_up(size_t(c + 1) * 4) + align_up(size_t(c) * 4) * 2;
+  };
+  ArWorkspace w{};
+  size_t off = 0;
+  w.meta1 = off; off += meta_bytes(T);
+  w.hid1 = off;  off += align_up(size_t(T) * H * eb);
+  w.metak = off; off += meta_bytes(c);
+  w.hidk = off;  off += align_up(size_t(c) * H * eb);
+  w.tok = off;   off += align_up(size_t(c) * 4);
+  const size_t f1 = plan_workspace(m, c, 1, T).total, fk = plan_workspace(m, c, 1, c).total;
+  w.fwd_bytes = f1 > fk ? f1 : fk;
+  w.fwd = off;   off += w.fwd_bytes;
+  w.total = off;
+  return w;
+}
+struct MetaView {
+  int32_t *ids, *pos;
+  int64_t* slot;
+  uint8_t *rej, *msk;
+  int32_t *hmap, *cu, *kvl, *sidx;
+};
+MetaView carve_meta(char* base, size_t rows, int c) {
+  MetaView v{};
+  size_t off = 0;
+  v.ids = reinterpret_cast<int32_t*>(base + off);  off += align_up(rows * 4);
+  v.pos = reinterpret_cast<int32_t*>(base + off);  off += align_up(rows * 4);
+  v.slot = reinterpret_cast<int64_t*>(base + off); off += align_up(rows * 8);
+  v.rej = reinterpret_cast<uint8_t*>(base + off);  off += align_up(rows);
+  v.msk = reinterpret_cast<uint8_t*>(base + off);  off += align_up(rows);
+  v.hmap = reinterpret_cast<int32_t*>(base + off); off += align_up(rows * 4);
+  v.cu = reinterpret_cast<int32_t*>(base + off);   off += align_up(size_t(c + 1) * 4);
+  v.kvl = reinterpret_cast<int32_t*>(base + off);  off += align_up(size_t(c) * 4);
+  v.sidx = reinterpret_cast<int32_t*>(base + off);
+  return v;
+}
+}  // namespace
+
+size_t pe_autoregressive_workspace_bytes(const pe_model* m, int32_t c, int32_t K, int32_t T) {
+  if (!m || c <= 0 || K <= 0 || T < c) return 0;
+  return plan_ar(m, c, T).total;
+}
+
+pe_status pe_draft_autoregressive(const pe_model* m, int32_t c, int32_t K, int32_t T,
+                                  const int32_t* query_lens, const int32_t* target_ids,
+                                  const int32_t* target_pos, const int32_t* num_accepted,
+                                  const int32_t* bonus_ids, const void* target_hidden,
+                                  const int32_t* block_table, int32_t max_blocks, void* const* k_cache,
+                                  void* const* v_cache, void* workspace, size_t workspace_bytes,
+                                  int32_t* draft_tokens, hipStream_t stream) {
+  if (!m || c <= 0 || K <= 0 || T < c || max_blocks <= 0 || !workspace || !draft_tokens) return PE_EINVAL;
+  if (m->d.n_layers <= 0) return PE_EUNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return PE_EINVAL;
+  const ArWorkspace ws = plan_ar(m, c, T);
+  if (workspace_bytes < ws.total) return PE_EWORKSPACE;
+  char* wb = static_cast<char*>(workspace);
+  const MetaView m1 = carve_meta(wb + ws.meta1, size_t(T), c);
+  const MetaView mk = carve_meta(wb + ws.metak, size_t(c), c);
+  int32_t* tok = reinterpret_cast<int32_t*>(wb + ws.tok);
+  void* fwd = wb + ws.fwd;
+  pe_status st;
+  // pass 1: the verified rows with the bonus token, no MASK rows (one token)
+  if ((st = pe_prepare_draft_batch(m, c, 1, T, query_lens, target_ids, target_pos, num_accepted, bonus_ids,
+                                   target_hidden, block_table, max_blocks, m1.ids, m1.pos, m1.slot, m1.rej,
+                                   m1.msk, m1.hmap, m1.cu, m1.kvl, m1.sidx, wb + ws.hid1, stream)) != PE_OK)
+    return st;
+  if ((st = pe_draft_forward(m, c, 1, T, m1.ids, m1.pos, m1.slot, m1.rej, m1.cu, m1.kvl, m1.sidx,
+                             wb + ws.hid1, block_table, max_blocks, k_cache, v_cache, fwd, ws.fwd_bytes, tok,
+                             nullptr, nullptr, stream)) != PE_OK)
+    return st;
+  // passes 2..K: one row per sequence fed with its own previous token and
+  // final residual (the drafter workspace's residual region sits at offset 0)
+  for (int k = 1; k <= K; ++k) {
+    pe::ArStepArgs a{};
+    a.c = c; a.K = K; a.k = k; a.H = m->d.hidden; a.max_blocks = max_blocks; a.last = k == K;
+    a.dtype = dt(m); a.prev_tokens = tok; a.x = reinterpret_cast<const float*>(fwd);
+    a.prev_sample_idx = k == 1 ? m1.sidx : nullptr; a.base_kv_lens = m1.kvl; a.block_table = block_table;
+    a.draft_tokens = draft_tokens; a.ids = mk.ids; a.pos = mk.pos; a.slot = mk.slot; a.rejected = mk.rej;
+    a.cu_draft = mk.cu; a.kv_lens = mk.kvl; a.sample_idx = mk.sidx; a.hidden = wb + ws.hidk;
+    PE_HIP(pe::launch_ar_step(a, stream));
+    if (k == K) break;
+    if ((st = pe_draft_forward(m, c, 1, c, mk.ids, mk.pos, mk.slot, mk.rej, mk.cu, mk.kvl, mk.sidx,
+                               wb + ws.hidk, block_table, max_blocks, k_cache, v_cache, fwd, ws.fwd_bytes, tok,
+                               nullptr, nullptr, stream)) != PE_OK)
+      return st;
+  }
+  return PE_OK;
+}
+
+pe_status pe_next_verified_batch(int32_t c, int32_t K, const int32_t* kv_lens, const int32_t* bonus_ids,
+                                 const int32_t* draft_tokens, const int32_t* num_accepted_next,
+                                 const int32_t* bonus_next, int32_t* query_lens_out, int32_t* target_ids_out,
+                                 int32_t* target_pos_out, int32_t* num_accepted_out, int32_t* bonus_ids_out,
+                                 hipStream_t stream) {
+  if (c <= 0 || K <= 0) return PE_EINVAL;
+  const void* ptrs[] = {kv_lens, bonus_ids, draft_tokens, num_accepted_next, bonus_next, query_lens_out,
+                        target_ids_out, target_pos_out, num_accepted_out, bonus_ids_out};
+  for (const void* p : ptrs)
+    if (!p) return PE_EINVAL;
+  PE_HIP(pe::launch_next_batch(c, K, kv_lens, bonus_ids, draft_tokens, num_accepted_next, bonus_next,
+                               query_lens_out, target_ids_out, target_pos_out, num_accepted_out, bonus_ids_out,
+                               stream));
+  return PE_OK;
+}
+
 pe_status pe_accept(int32_t c, int32_t K, const int32_t* draft, const int32_t* target, int32_t* acc,
                     int32_t* bonus, hipStream_t stream) {
   if (c <= 0 || K <= 0 || !draft || !target || !acc || !bonus) return PE_EINVAL;

@@ -138,6 +138,29 @@ struct AttnArgs {
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
+// Autoregressive baseline: store token k-1 and build the single row of pass k.
+struct ArStepArgs {
+  int c, K, k, H, max_blocks;
+  bool last;                    // only store the final token
+  DType dtype;
+  const int32_t* prev_tokens;   // [c] tokens of pass k-1
+  const float* x;               // residual rows of pass k-1 [rows, H]
+  const int32_t* prev_sample_idx;  // rows of x that produced the tokens (null: row i)
+  const int32_t* base_kv_lens;  // [c] kv lengths of the one-token first pass (= bonus position + 1)
+  const int32_t* block_table;
+  int32_t* draft_tokens;        // [c, K]
+  int32_t *ids, *pos;
+  int64_t* slot;
+  uint8_t* rejected;
+  int32_t *cu_draft, *kv_lens, *sample_idx;
+  void* hidden;                 // [c, H] model dtype
+};
+hipError_t launch_ar_step(const ArStepArgs& a, hipStream_t s);
+hipError_t launch_next_batch(int c, int K, const int32_t* kv_lens, const int32_t* bonus, const int32_t* drafts,
+                             const int32_t* acc_next, const int32_t* bonus_next, int32_t* query_lens,
+                             int32_t* target_ids, int32_t* target_pos, int32_t* num_accepted, int32_t* bonus_ids,
+                             hipStream_t s);
+
 hipError_t launch_argmax_finalize(int S, int parts, const Top2* partials, int32_t* tokens,
                                   float* gap, hipStream_t s);
 hipError_t launch_accept(int c, int K, const int32_t* draft, const int32_t* target,

@@ -11,6 +11,8 @@
  *   pe_draft_forward        fc(emb ++ h) -> decoder layer(s) over the paged KV
  *                           cache -> LM head -> argmax, for all K drafts at once;
  *   pe_accept               greedy accepted length against target tokens.
+ *   pe_draft_autoregressive the K-pass autoregressive baseline on the same kernels.
+ *   pe_next_verified_batch  next round's verified batch from this round's results.
  *
  * Sources (page title, section):
  *   [PF] "P-EAGLE: Faster LLM Inference with Parallel Speculative Decoding in
@@ -191,6 +193,59 @@ pe_status pe_draft_forward(const pe_model *model, int32_t num_seqs, int32_t K, i
 pe_status pe_accept(int32_t num_seqs, int32_t K, const int32_t *draft_tokens,
                     const int32_t *target_tokens, int32_t *num_accepted, int32_t *bonus_ids,
                     hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Autoregressive baseline on the same kernels ("P-EAGLE: Parallel Speculative
+ * Decoding in vLLM", Solving the Autoregressive Drafting Bottleneck: EAGLE-style
+ * drafters need one forward pass per draft token, so drafting latency grows
+ * with K; P-EAGLE replaces the K passes by one).
+ *
+ * Pass 1 is the parallel-draft pass with K = 1 over the verified batch (the
+ * bonus row, no MASK rows) and yields token 0.  Pass k = 1..K-1 runs one row
+ * per sequence: token k-1 at position base_i + k (base_i = position of the
+ * bonus row), with the drafter's own final residual (pre final RMSNorm) of the
+ * row that produced token k-1 as hidden input, rounded to the model dtype; its
+ * (k, v) are appended to the cache at that position and the row yields token k.
+ *
+ *   inputs: the verified batch exactly as for pe_prepare_draft_batch; the
+ *           block table must cover positions up to base_i + K - 1
+ *   k_cache, v_cache: HOST arrays [n_layers] of device caches (read and written)
+ *   workspace: device scratch of at least pe_autoregressive_workspace_bytes(
+ *              model, c, K, T) bytes, 256-byte aligned
+ *   draft_tokens[c*K]  int32 output, sequence-major
+ * Returns PE_EWORKSPACE for a short workspace; otherwise as pe_draft_forward.
+ * Launches K forward passes plus small row builders on the stream; nothing is
+ * synchronized on the host.
+ * ------------------------------------------------------------------------- */
+size_t pe_autoregressive_workspace_bytes(const pe_model *model, int32_t num_seqs, int32_t K,
+                                         int32_t total_target_rows);
+pe_status pe_draft_autoregressive(const pe_model *model, int32_t num_seqs, int32_t K,
+                                  int32_t total_target_rows, const int32_t *query_lens,
+                                  const int32_t *target_ids, const int32_t *target_pos,
+                                  const int32_t *num_accepted, const int32_t *bonus_ids,
+                                  const void *target_hidden, const int32_t *block_table,
+                                  int32_t max_blocks, void *const *k_cache, void *const *v_cache,
+                                  void *workspace, size_t workspace_bytes, int32_t *draft_tokens,
+                                  hipStream_t stream);
+
+/* Next round's verified batch, on the device ("P-EAGLE: Faster LLM Inference
+ * with Parallel Speculative Decoding in vLLM", 怎么做的: each round drafts K
+ * tokens that the target model then verifies).  The target verified, for
+ * sequence i, the K + 1 rows [bonus_ids[i], draft_tokens[i*K .. i*K+K-1]] at
+ * positions base_i + 1 .. base_i + K + 1, where base_i = kv_lens[i] - K is the
+ * position of this round's bonus row (kv_lens as produced by
+ * pe_prepare_draft_batch for this round), and accepted num_accepted_next[i]
+ * drafts with new bonus bonus_next[i] (pe_accept's outputs).
+ *   outputs: query_lens_out[c] = K + 1; target_ids_out / target_pos_out
+ *   [c*(K+1)]; num_accepted_out[c], bonus_ids_out[c] copies of the inputs.
+ * The target hidden states of those rows come from the verifier.  Inputs and
+ * outputs may not alias. */
+pe_status pe_next_verified_batch(int32_t num_seqs, int32_t K, const int32_t *kv_lens,
+                                 const int32_t *bonus_ids, const int32_t *draft_tokens,
+                                 const int32_t *num_accepted_next, const int32_t *bonus_next,
+                                 int32_t *query_lens_out, int32_t *target_ids_out,
+                                 int32_t *target_pos_out, int32_t *num_accepted_out,
+                                 int32_t *bonus_ids_out, hipStream_t stream);
 
 /* Static description of a status code. */
 const char *pe_status_string(pe_status status);

@@ -13,6 +13,7 @@ independent library compositions); see ``tests/test_oracle_*.py``.
 from .peagle_oracle import (  # noqa: F401
     PADDING_SLOT_ID,
     decode,
+    encode,
     round_operand,
     expand_batch,
     scatter_broadcast,
@@ -23,4 +24,7 @@ from .peagle_oracle import (  # noqa: F401
     draft_forward,
     accept,
     parallel_draft_step,
+    apply_cache_writes,
+    next_verified_batch,
+    autoregressive_draft,
 )

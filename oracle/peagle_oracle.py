@@ -377,6 +377,103 @@ def accept(draft_tokens: np.ndarray, target_tokens: np.ndarray):
 
 
 # ----------------------------------------------------------------------------
+# cache state across passes and rounds
+# ----------------------------------------------------------------------------
+def apply_cache_writes(spec, k_cache: Sequence[np.ndarray], v_cache: Sequence[np.ndarray],
+                       cache_writes) -> None:
+    """Store one pass's (k, v) writes into the caches (in place), in the
+    cache dtype.  ``draft_forward`` overlays a pass's own writes when it reads
+    the cache but leaves the arrays untouched; passes that build on earlier
+    ones (the autoregressive baseline, later rounds) commit them here."""
+    bs = spec.block_size
+    for li, w in enumerate(cache_writes):
+        sl = np.asarray(w["slots"], dtype=np.int64)
+        if len(sl) == 0:
+            continue
+        k_cache[li][sl // bs, :, sl % bs, :] = encode(np.asarray(w["k"]), spec.dtype)
+        v_cache[li][sl // bs, :, sl % bs, :] = encode(np.asarray(w["v"]), spec.dtype)
+
+
+def next_verified_batch(kv_lens, bonus_ids, draft_tokens, num_accepted_next, bonus_next, K: int) -> dict:
+    """The batch the next round drafts from ([PF] "怎么做的": every round the
+    K drafts are verified by the target).  For sequence i the verifier saw
+    the K+1 rows [bonus_i, d_0 .. d_{K-1}] at positions base_i+1 .. base_i+K+1
+    (base_i = kv_lens[i] - K, the position of this round's bonus row) and
+    kept num_accepted_next[i] drafts, with bonus_next[i] as the new bonus."""
+    kv_lens = np.asarray(kv_lens, dtype=np.int64)
+    drafts = np.asarray(draft_tokens, dtype=np.int64).reshape(len(kv_lens), K)
+    ids, pos = [], []
+    for i in range(len(kv_lens)):
+        base = int(kv_lens[i]) - K
+        ids.append(np.concatenate([[int(bonus_ids[i])], drafts[i]]))
+        pos.append(base + 1 + np.arange(K + 1))
+    c = len(kv_lens)
+    return dict(query_lens=np.full(c, K + 1, np.int32), target_ids=np.concatenate(ids).astype(np.int32),
+                target_pos=np.concatenate(pos).astype(np.int32),
+                num_accepted=np.asarray(num_accepted_next, dtype=np.int32).copy(),
+                bonus_ids=np.asarray(bonus_next, dtype=np.int32).copy())
+
+
+# ----------------------------------------------------------------------------
+# autoregressive baseline
+# ----------------------------------------------------------------------------
+def autoregressive_draft(spec, weights: dict, batch, K: int, precision: str = "mirror",
+                         seqs: Optional[Sequence[int]] = None, forced_tokens: Optional[np.ndarray] = None) -> dict:
+    """K drafts from K sequential one-token passes, the drafting scheme whose
+    latency grows with K ([PP] "Solving the Autoregressive Drafting
+    Bottleneck").
+
+    Pass 0 is the parallel-draft pass with K = 1 over the verified batch (the
+    bonus row, no MASK rows).  Pass k >= 1 has one row per sequence: token
+    k-1 at position base+k (base = position of the bonus row), its hidden
+    input being the drafter's own final residual (before the final RMSNorm)
+    of the row that produced token k-1, stored in the model dtype -- the
+    pages do not say which feature an autoregressive drafter feeds back; this
+    reading takes the drafter's last hidden state.  Each pass's cache writes
+    are committed before the next pass.
+
+    ``forced_tokens`` [c, K] feeds those tokens forward instead of the
+    oracle's own argmax (teacher forcing against another implementation's
+    drafts).  Returns tokens and logits per step and the final caches.
+    """
+    dt = spec.dtype
+    c = len(batch.query_lens)
+    seqs = list(range(c)) if seqs is None else [int(i) for i in seqs]
+    kc = [np.array(k, copy=True) for k in batch.k_cache]
+    vc = [np.array(v, copy=True) for v in batch.v_cache]
+    last = f"x{spec.n_layers - 1}"
+    meta = expand_batch(batch.query_lens, batch.target_ids, batch.target_pos, batch.num_accepted,
+                        batch.bonus_ids, batch.block_table, 1, spec.mask_token_id, spec.block_size)
+    hd = scatter_broadcast(batch.target_hidden, meta["hidden_map"], meta["is_masked"], weights["h_shared"],
+                           len(meta["draft_ids"]))
+    base = np.asarray(meta["kv_lens"], dtype=np.int64) - 1
+    tokens = np.zeros((len(seqs), K), np.int64)
+    logits = []
+    for k in range(K):
+        f = draft_forward(spec, weights, meta, hd, batch.block_table, kc, vc, 1, precision=precision, seqs=seqs)
+        apply_cache_writes(spec, kc, vc, f["cache_writes"])
+        tokens[:, k] = f["tokens"][:, 0]
+        logits.append(f["logits"][:, 0])
+        if k == K - 1:
+            break
+        feed = tokens[:, k] if forced_tokens is None else np.asarray(forced_tokens)[seqs, k]
+        local = {int(r): n for n, r in enumerate(f["rows"])}
+        xs = f["intermediates"][last][[local[int(meta["sample_idx"][i])] for i in seqs]]
+        ids = np.zeros(c, np.int32)
+        hid = np.zeros((c, spec.hidden), dtype=np.uint16 if dt == "bf16" else np.float32)
+        ids[seqs] = feed
+        hid[seqs] = encode(xs, dt)
+        pos = (base + k + 1).astype(np.int32)
+        slot = np.array([_slots_of(np.asarray(batch.block_table[i], dtype=np.int64), np.array([pos[i]]),
+                                   spec.block_size)[0] for i in range(c)], dtype=np.int64)
+        meta = dict(draft_ids=ids, draft_pos=pos, slot_mapping=slot, is_rejected=np.zeros(c, np.uint8),
+                    is_masked=np.zeros(c, np.uint8), cu_draft=np.arange(c + 1, dtype=np.int32),
+                    kv_lens=(pos.astype(np.int64) + 1).astype(np.int32), sample_idx=np.arange(c, dtype=np.int32))
+        hd = hid
+    return dict(tokens=tokens, logits=np.stack(logits, axis=1), k_cache=kc, v_cache=vc, seqs=np.array(seqs))
+
+
+# ----------------------------------------------------------------------------
 # whole round
 # ----------------------------------------------------------------------------
 def parallel_draft_step(spec, weights: dict, batch, precision: str = "mirror",

@@ -178,6 +178,11 @@ def _workloads() -> dict:
         seed=2, weight_seed=2,
         description="GPT-OSS-20B-shaped drafter (H=2880, 64x64 q heads, 8 kv heads, I=7680, "
                     "V=201088), c=1, K=7, 2048 cached tokens")
+    for k in (3, 5):
+        w[f"gptoss20b-bf16-c1-k{k}"] = Workload(
+            f"gptoss20b-bf16-c1-k{k}", GPTOSS20B, c=1, K=k, ctx_lo=2048, ctx_hi=2048, accept_hi=k,
+            seed=2, weight_seed=2,
+            description=f"GPT-OSS-20B-shaped drafter, c=1, K={k}, 2048 cached tokens (depth sweep)")
     w["gptoss20b-bf16-c64-k7"] = Workload(
         "gptoss20b-bf16-c64-k7", GPTOSS20B, c=64, K=7, ctx_lo=512, ctx_hi=8192, accept_hi=7,
         seed=3, weight_seed=2,
@@ -270,10 +275,12 @@ def _canary(dtype: str):
 
 
 def make_batch(wl: Workload, seed: Optional[int] = None, with_cache: Optional[bool] = None,
-               accepted: Optional[np.ndarray] = None) -> Batch:
+               accepted: Optional[np.ndarray] = None, extra_positions: int = 0) -> Batch:
     """Verified batch for one parallel-draft round of workload ``wl``.
 
-    ``accepted`` overrides the drawn a_i (used by exhaustive sweeps).
+    ``accepted`` overrides the drawn a_i (used by exhaustive sweeps);
+    ``extra_positions`` extends every block table (and the NaN-filled pages
+    behind it) that many positions further, for later rounds.
     """
     spec = wl.model
     seed = wl.seed if seed is None else seed
@@ -294,7 +301,7 @@ def make_batch(wl: Workload, seed: Optional[int] = None, with_cache: Optional[bo
 
     bs = spec.block_size
     # blocks cover every position a draft row can occupy: P_i .. P_i + L + K - 2
-    need = [int(-(-(P[i] + L + K - 1) // bs)) for i in range(c)]
+    need = [int(-(-(P[i] + L + K - 1 + extra_positions) // bs)) for i in range(c)]
     total = int(sum(need))
     perm = rng.permutation(total).astype(np.int32)
     max_blocks = max(need)

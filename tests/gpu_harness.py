@@ -16,6 +16,12 @@ LOGIT_TOL = {"fp32": 1e-5, "bf16": 2e-2}
 DEV = "cuda:0"
 
 
+def _say(msg):
+    """Progress line for the GPU logs (flushed: a fault must not swallow it)."""
+    print(msg, flush=True)
+
+
+
 @functools.lru_cache(maxsize=4)
 def host_weights(spec, wseed, prep_only=False):
     return synth.make_weights(spec, wseed, prep_only=prep_only)
