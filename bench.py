@@ -120,6 +120,8 @@ def main() -> int:
     ap.add_argument("--mode", choices=("peagle", "ar", "loop"), default="peagle",
                     help="peagle: one parallel-draft round per step; ar: the K-pass autoregressive baseline "
                          "on the same kernels; loop: rounds chained through the device-built next batch")
+    ap.add_argument("--layout", choices=("fixed", "compact"), default="fixed",
+                    help="draft layout: fixed (rejected rows kept as inert rows) or compact (dropped)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy five times (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -149,8 +151,10 @@ def main() -> int:
     rng = __import__("numpy").random.default_rng(wl.seed + 99)
     tgt = to_torch(rng.integers(0, spec.vocab - 1, size=(wl.c, wl.K + 1)), device=dev)
     c, K, T, N = wl.c, wl.K, b.T, b.N
+    compact = args.layout == "compact"
     prep = pe.prepare_draft_batch(model, K, db["query_lens"], db["target_ids"], db["target_pos"],
-                                  db["num_accepted"], db["bonus_ids"], db["target_hidden"], db["block_table"])
+                                  db["num_accepted"], db["bonus_ids"], db["target_hidden"], db["block_table"],
+                                  compact=compact)
     ws = torch.empty(model.workspace_bytes(c, K, N), dtype=torch.uint8, device=dev)
     tokens = torch.empty((c, K), dtype=torch.int32, device=dev)
     acc = torch.empty(c, dtype=torch.int32, device=dev)
@@ -162,7 +166,8 @@ def main() -> int:
 
     def step():
         pe.prepare_draft_batch(model, K, db["query_lens"], db["target_ids"], db["target_pos"], db["num_accepted"],
-                               db["bonus_ids"], db["target_hidden"], db["block_table"], out=prep, stream=stream)
+                               db["bonus_ids"], db["target_hidden"], db["block_table"], out=prep, stream=stream,
+                               compact=compact)
         pe.draft_forward(model, prep, db["block_table"], db["k_cache"], db["v_cache"], workspace=ws,
                          tokens=tokens, stream=stream)
         pe.accept(tokens, tgt, acc, bonus, stream=stream)
@@ -186,7 +191,7 @@ def main() -> int:
         def step():  # noqa: F811
             pe.prepare_draft_batch(model, K, cur["query_lens"], cur["target_ids"], cur["target_pos"],
                                    cur["num_accepted"], cur["bonus_ids"], hid_next, db["block_table"], out=prep,
-                                   stream=stream)
+                                   stream=stream, compact=compact)
             pe.draft_forward(model, prep, db["block_table"], db["k_cache"], db["v_cache"], workspace=ws,
                              tokens=tokens, stream=stream)
             pe.accept(tokens, tgt, acc, bonus, stream=stream)
@@ -221,7 +226,7 @@ def main() -> int:
         with torch.cuda.graph(graph):
             pe.prepare_draft_batch(model, K, db["query_lens"], db["target_ids"], db["target_pos"],
                                    db["num_accepted"], db["bonus_ids"], db["target_hidden"], db["block_table"],
-                                   out=prep)
+                                   out=prep, compact=compact)
             pe.draft_forward(model, prep, db["block_table"], db["k_cache"], db["v_cache"], workspace=ws,
                              tokens=tokens)
             pe.accept(tokens, tgt, acc, bonus)
@@ -261,6 +266,7 @@ def main() -> int:
         "ms_per_step": round(ms_per_step, 5),
         "launch_mode": mode,
         "mode": args.mode,
+        "layout": args.layout,
         "eager_ms_per_step": round(eager_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",

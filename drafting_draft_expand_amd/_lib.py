@@ -23,7 +23,8 @@ PE_KERNEL_LM_HEAD, PE_KERNEL_PREPARE, PE_KERNEL_ATTENTION = 0, 1, 2
 
 EXPORTED = ("pe_model_create", "pe_model_destroy", "pe_workspace_bytes", "pe_prepare_draft_batch",
             "pe_draft_forward", "pe_accept", "pe_status_string", "pe_timing_enable", "pe_timing_read",
-            "pe_autoregressive_workspace_bytes", "pe_draft_autoregressive", "pe_next_verified_batch")
+            "pe_autoregressive_workspace_bytes", "pe_draft_autoregressive", "pe_next_verified_batch",
+            "pe_prepare_draft_batch_compact")
 
 
 class PeError(RuntimeError):
@@ -70,6 +71,8 @@ def load() -> ctypes.CDLL:
     lib.pe_workspace_bytes.restype = SZ
     lib.pe_prepare_draft_batch.argtypes = [P, I32, I32, I32] + [P] * 7 + [I32] + [P] * 10 + [P]
     lib.pe_prepare_draft_batch.restype = I32
+    lib.pe_prepare_draft_batch_compact.argtypes = lib.pe_prepare_draft_batch.argtypes
+    lib.pe_prepare_draft_batch_compact.restype = I32
     lib.pe_draft_forward.argtypes = [P, I32, I32, I32] + [P] * 9 + [I32] + [P, P, P, SZ] + [P, P, P] + [P]
     lib.pe_draft_forward.restype = I32
     lib.pe_accept.argtypes = [I32, I32, P, P, P, P, P]
@@ -176,8 +179,10 @@ class DraftModel:
 def prepare_draft_batch(model: DraftModel, K: int, query_lens: torch.Tensor, target_ids: torch.Tensor,
                         target_pos: torch.Tensor, num_accepted: torch.Tensor, bonus_ids: torch.Tensor,
                         target_hidden: torch.Tensor, block_table: torch.Tensor,
-                        out: Optional[Dict[str, torch.Tensor]] = None, stream=None) -> Dict[str, torch.Tensor]:
-    """Expand the verified batch (see pe_prepare_draft_batch).  Returns the draft batch tensors."""
+                        out: Optional[Dict[str, torch.Tensor]] = None, stream=None,
+                        compact: bool = False) -> Dict[str, torch.Tensor]:
+    """Expand the verified batch (see pe_prepare_draft_batch; compact=True:
+    pe_prepare_draft_batch_compact).  Returns the draft batch tensors."""
     c = int(query_lens.numel())
     T = int(target_ids.numel())
     N = T + c * (K - 1)
@@ -191,13 +196,14 @@ def prepare_draft_batch(model: DraftModel, K: int, query_lens: torch.Tensor, tar
                    hidden_map=torch.empty(T, **i32), cu_draft=torch.empty(c + 1, **i32),
                    kv_lens=torch.empty(c, **i32), sample_idx=torch.empty(c * K, **i32),
                    draft_hidden=torch.empty((N, target_hidden.shape[1]), dtype=target_hidden.dtype, device=dev))
-    st = load().pe_prepare_draft_batch(
+    fn = load().pe_prepare_draft_batch_compact if compact else load().pe_prepare_draft_batch
+    st = fn(
         model.handle, c, K, T, _ptr(query_lens), _ptr(target_ids), _ptr(target_pos), _ptr(num_accepted),
         _ptr(bonus_ids), _ptr(target_hidden), _ptr(block_table), int(block_table.shape[1]),
         _ptr(out["draft_ids"]), _ptr(out["draft_pos"]), _ptr(out["slot_mapping"]), _ptr(out["is_rejected"]),
         _ptr(out["is_masked"]), _ptr(out["hidden_map"]), _ptr(out["cu_draft"]), _ptr(out["kv_lens"]),
         _ptr(out["sample_idx"]), _ptr(out["draft_hidden"]), _stream(stream))
-    _check(st, "pe_prepare_draft_batch")
+    _check(st, "pe_prepare_draft_batch_compact" if compact else "pe_prepare_draft_batch")
     out["num_seqs"], out["K"], out["num_rows"] = c, K, N
     return out
 

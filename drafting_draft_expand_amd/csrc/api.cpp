@@ -220,15 +220,14 @@ size_t pe_workspace_bytes(const pe_model* m, int32_t c, int32_t K, int32_t N) {
   return plan_workspace(m, c, K, N).total;
 }
 
-pe_status pe_prepare_draft_batch(const pe_model* m, int32_t c, int32_t K, int32_t T,
-                                 const int32_t* query_lens, const int32_t* target_ids,
-                                 const int32_t* target_pos, const int32_t* num_accepted,
-                                 const int32_t* bonus_ids, const void* target_hidden,
-                                 const int32_t* block_table, int32_t max_blocks, int32_t* draft_ids,
-                                 int32_t* draft_pos, int64_t* slot_mapping, uint8_t* is_rejected,
-                                 uint8_t* is_masked, int32_t* hidden_map, int32_t* cu_draft,
-                                 int32_t* kv_lens, int32_t* sample_idx, void* draft_hidden,
-                                 hipStream_t stream) {
+namespace {
+pe_status prepare_impl(const pe_model* m, int32_t c, int32_t K, int32_t T, const int32_t* query_lens,
+                       const int32_t* target_ids, const int32_t* target_pos, const int32_t* num_accepted,
+                       const int32_t* bonus_ids, const void* target_hidden, const int32_t* block_table,
+                       int32_t max_blocks, int32_t* draft_ids, int32_t* draft_pos, int64_t* slot_mapping,
+                       uint8_t* is_rejected, uint8_t* is_masked, int32_t* hidden_map, int32_t* cu_draft,
+                       int32_t* kv_lens, int32_t* sample_idx, void* draft_hidden, hipStream_t stream,
+                       int compact) {
   if (!m || c <= 0 || K <= 0 || T < c || max_blocks <= 0) return PE_EINVAL;
   const void* ptrs[] = {query_lens, target_ids, target_pos, num_accepted, bonus_ids, target_hidden,
                         block_table, draft_ids, draft_pos, slot_mapping, is_rejected, is_masked,
@@ -248,9 +247,39 @@ pe_status pe_prepare_draft_batch(const pe_model* m, int32_t c, int32_t K, int32_
   a.draft_ids = draft_ids; a.draft_pos = draft_pos; a.slot_mapping = slot_mapping;
   a.is_rejected = is_rejected; a.is_masked = is_masked; a.hidden_map = hidden_map;
   a.cu_draft = cu_draft; a.kv_lens = kv_lens; a.sample_idx = sample_idx; a.draft_hidden = draft_hidden;
+  a.compact = compact;
   TimedScope ts(const_cast<pe_model*>(m), PE_KERNEL_PREPARE, stream);
   PE_HIP(pe::launch_prepare(a, stream));
   return PE_OK;
+}
+}  // namespace
+
+pe_status pe_prepare_draft_batch(const pe_model* m, int32_t c, int32_t K, int32_t T,
+                                 const int32_t* query_lens, const int32_t* target_ids,
+                                 const int32_t* target_pos, const int32_t* num_accepted,
+                                 const int32_t* bonus_ids, const void* target_hidden,
+                                 const int32_t* block_table, int32_t max_blocks, int32_t* draft_ids,
+                                 int32_t* draft_pos, int64_t* slot_mapping, uint8_t* is_rejected,
+                                 uint8_t* is_masked, int32_t* hidden_map, int32_t* cu_draft,
+                                 int32_t* kv_lens, int32_t* sample_idx, void* draft_hidden,
+                                 hipStream_t stream) {
+  return prepare_impl(m, c, K, T, query_lens, target_ids, target_pos, num_accepted, bonus_ids, target_hidden,
+                      block_table, max_blocks, draft_ids, draft_pos, slot_mapping, is_rejected, is_masked,
+                      hidden_map, cu_draft, kv_lens, sample_idx, draft_hidden, stream, 0);
+}
+
+pe_status pe_prepare_draft_batch_compact(const pe_model* m, int32_t c, int32_t K, int32_t T,
+                                         const int32_t* query_lens, const int32_t* target_ids,
+                                         const int32_t* target_pos, const int32_t* num_accepted,
+                                         const int32_t* bonus_ids, const void* target_hidden,
+                                         const int32_t* block_table, int32_t max_blocks, int32_t* draft_ids,
+                                         int32_t* draft_pos, int64_t* slot_mapping, uint8_t* is_rejected,
+                                         uint8_t* is_masked, int32_t* hidden_map, int32_t* cu_draft,
+                                         int32_t* kv_lens, int32_t* sample_idx, void* draft_hidden,
+                                         hipStream_t stream) {
+  return prepare_impl(m, c, K, T, query_lens, target_ids, target_pos, num_accepted, bonus_ids, target_hidden,
+                      block_table, max_blocks, draft_ids, draft_pos, slot_mapping, is_rejected, is_masked,
+                      hidden_map, cu_draft, kv_lens, sample_idx, draft_hidden, stream, 1);
 }
 
 pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, const int32_t* draft_ids,
@@ -296,6 +325,8 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
   const int cus = num_cus(m);
 
   const int ss_tiles = (H + 15) / 16;
+  // rows at and past cu_draft[c] are padding (compacted layout): skipped
+  const int32_t* live = cu_draft + c;
   const bool fused = fused_plan(d, N);
   const bool fnorm = fused && fused_final_norm(d, N, S);
   // attention and LM head are shared by both plans
@@ -320,7 +351,7 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
     // fc over [emb(id) ; h] gathered on the fly; epilogue emits row sums of squares
     {
       pe::GemvArgs g{};
-      g.M = N; g.Nout = H; g.K = 2 * H; g.amode = pe::AMode::Gather;
+      g.M = N; g.m_live = live; g.Nout = H; g.K = 2 * H; g.amode = pe::AMode::Gather;
       g.ids = draft_ids; g.embed = m->w.embed; g.x2 = draft_hidden;
       g.w_a = g.w_b = g.w_c = m->w.w_fc; g.n_a = H; g.n_b = 0;
       g.y = x; g.ldy = H;
@@ -330,11 +361,11 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
       const pe_layer_weights& L = m->layers[l];
       // RMSNorm as its own pass: forming it inside the projection would make
       // every workgroup re-read the fp32 rows (twice the operand traffic)
-      PE_HIP(pe::launch_rmsnorm(t, N, H, nullptr, x, L.ln1, d.rms_eps, act, stream));
+      PE_HIP(pe::launch_rmsnorm(t, N, H, nullptr, x, L.ln1, d.rms_eps, act, stream, live));
       {
         // q/k/v -> RoPE -> q operand + paged KV write
         pe::GemvArgs g{};
-        g.M = N; g.Nout = qd + 2 * kvd; g.K = H; g.amode = pe::AMode::Plain; g.x = act;
+        g.M = N; g.m_live = live; g.Nout = qd + 2 * kvd; g.K = H; g.amode = pe::AMode::Plain; g.x = act;
         g.w_a = L.wq; g.n_a = qd; g.w_b = L.wk; g.n_b = kvd; g.w_c = L.wv;
         g.rope.n_q = d.n_q; g.rope.n_kv = d.n_kv; g.rope.d = d.head_dim; g.rope.block_size = d.block_size;
         g.rope.freq = m->freq; g.rope.pos = draft_pos; g.rope.slot = slot_mapping;
@@ -345,22 +376,22 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
       if ((st = attention(l)) != PE_OK) return st;
       {
         pe::GemvArgs g{};
-        g.M = N; g.Nout = H; g.K = qd; g.amode = pe::AMode::Plain; g.x = act;
+        g.M = N; g.m_live = live; g.Nout = H; g.K = qd; g.amode = pe::AMode::Plain; g.x = act;
         g.w_a = g.w_b = g.w_c = L.wo; g.n_a = H; g.n_b = 0;
         g.y = x; g.ldy = H;
         if ((st = proj(g, pe::Epi::AddTo)) != PE_OK) return st;
       }
-      PE_HIP(pe::launch_rmsnorm(t, N, H, nullptr, x, L.ln2, d.rms_eps, act, stream));
+      PE_HIP(pe::launch_rmsnorm(t, N, H, nullptr, x, L.ln2, d.rms_eps, act, stream, live));
       {
         pe::GemvArgs g{};
-        g.M = N; g.Nout = d.inter; g.K = H; g.amode = pe::AMode::Plain; g.x = act;
+        g.M = N; g.m_live = live; g.Nout = d.inter; g.K = H; g.amode = pe::AMode::Plain; g.x = act;
         g.w_a = L.w_gate; g.w_b = L.w_up; g.w_c = L.w_up; g.n_a = d.inter; g.n_b = d.inter;
         g.y_op = mlp; g.ldy = d.inter;
         if ((st = proj(g, pe::Epi::SiluMul)) != PE_OK) return st;
       }
       {
         pe::GemvArgs g{};
-        g.M = N; g.Nout = H; g.K = d.inter; g.amode = pe::AMode::Plain; g.x = mlp;
+        g.M = N; g.m_live = live; g.Nout = H; g.K = d.inter; g.amode = pe::AMode::Plain; g.x = mlp;
         g.w_a = g.w_b = g.w_c = L.w_down; g.n_a = H; g.n_b = 0;
         g.y = x; g.ldy = H; g.ss_out = fnorm && l == d.n_layers - 1 ? ss0 : nullptr;
         if ((st = proj(g, pe::Epi::AddTo)) != PE_OK) return st;
@@ -370,17 +401,17 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
     PE_HIP(pe::launch_build_fc_input(t, N, H, draft_ids, m->w.embed, draft_hidden, act, stream));
     {
       pe::GemvArgs g{};
-      g.M = N; g.Nout = H; g.K = 2 * H; g.amode = pe::AMode::Plain; g.x = act;
+      g.M = N; g.m_live = live; g.Nout = H; g.K = 2 * H; g.amode = pe::AMode::Plain; g.x = act;
       g.w_a = m->w.w_fc; g.n_a = H; g.w_b = g.w_c = m->w.w_fc; g.n_b = 0;
       g.y = x; g.ldy = H;
       if ((st = proj(g, pe::Epi::Store)) != PE_OK) return st;
     }
     for (int l = 0; l < d.n_layers; ++l) {
       const pe_layer_weights& L = m->layers[l];
-      PE_HIP(pe::launch_rmsnorm(t, N, H, nullptr, x, L.ln1, d.rms_eps, act, stream));
+      PE_HIP(pe::launch_rmsnorm(t, N, H, nullptr, x, L.ln1, d.rms_eps, act, stream, live));
       {
         pe::GemvArgs g{};
-        g.M = N; g.Nout = qd + 2 * kvd; g.K = H; g.amode = pe::AMode::Plain; g.x = act;
+        g.M = N; g.m_live = live; g.Nout = qd + 2 * kvd; g.K = H; g.amode = pe::AMode::Plain; g.x = act;
         g.w_a = L.wq; g.n_a = qd; g.w_b = L.wk; g.n_b = kvd; g.w_c = L.wv;
         g.y = qkv; g.ldy = qd + 2 * kvd;
         if ((st = proj(g, pe::Epi::Store)) != PE_OK) return st;
@@ -395,22 +426,22 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
       if ((st = attention(l)) != PE_OK) return st;
       {
         pe::GemvArgs g{};
-        g.M = N; g.Nout = H; g.K = qd; g.amode = pe::AMode::Plain; g.x = act;
+        g.M = N; g.m_live = live; g.Nout = H; g.K = qd; g.amode = pe::AMode::Plain; g.x = act;
         g.w_a = g.w_b = g.w_c = L.wo; g.n_a = H; g.n_b = 0;
         g.y = x; g.ldy = H;
         if ((st = proj(g, pe::Epi::AddTo)) != PE_OK) return st;
       }
-      PE_HIP(pe::launch_rmsnorm(t, N, H, nullptr, x, L.ln2, d.rms_eps, act, stream));
+      PE_HIP(pe::launch_rmsnorm(t, N, H, nullptr, x, L.ln2, d.rms_eps, act, stream, live));
       {
         pe::GemvArgs g{};
-        g.M = N; g.Nout = d.inter; g.K = H; g.amode = pe::AMode::Plain; g.x = act;
+        g.M = N; g.m_live = live; g.Nout = d.inter; g.K = H; g.amode = pe::AMode::Plain; g.x = act;
         g.w_a = L.w_gate; g.w_b = L.w_up; g.w_c = L.w_up; g.n_a = d.inter; g.n_b = d.inter;
         g.y_op = mlp; g.ldy = d.inter;
         if ((st = proj(g, pe::Epi::SiluMul)) != PE_OK) return st;
       }
       {
         pe::GemvArgs g{};
-        g.M = N; g.Nout = H; g.K = d.inter; g.amode = pe::AMode::Plain; g.x = mlp;
+        g.M = N; g.m_live = live; g.Nout = H; g.K = d.inter; g.amode = pe::AMode::Plain; g.x = mlp;
         g.w_a = g.w_b = g.w_c = L.w_down; g.n_a = H; g.n_b = 0;
         g.y = x; g.ldy = H;
         if ((st = proj(g, pe::Epi::AddTo)) != PE_OK) return st;

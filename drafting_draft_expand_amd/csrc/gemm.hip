@@ -215,6 +215,7 @@ __global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel
   if (L >= total) return;
   const int mt = L % num_m, nt = L / num_m;
   const int m0 = mt * BM;
+  if (a.m_live && m0 >= *a.m_live) return;  // only padding rows in this tile
   const int nk = a.K / BK;
 
   // thread -> 16-byte chunk mapping of the A and W tiles (rows of CPR chunks);

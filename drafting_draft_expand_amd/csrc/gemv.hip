@@ -230,6 +230,7 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
   const int ks0 = min(KS, wave * per);
   const int ks1 = min(KS, ks0 + per);
   const int m0 = blockIdx.y * 16;
+  if (a.m_live && m0 >= *a.m_live) return;  // only padding rows in this slice
   const int mrow = m0 + (lane & 15);
   const bool xvalid = mrow < a.M;
   const int mclamp = min(mrow, a.M - 1);

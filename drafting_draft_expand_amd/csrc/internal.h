@@ -28,6 +28,7 @@ struct RopeFreq {
 // ---------------------------------------------------------------- expansion
 struct PrepareArgs {
   int c, K, T, N, H, block_size, max_blocks, mask_id;
+  int compact;                  // drop rejected rows (padding after the live rows)
   DType dtype;
   const int32_t *query_lens, *target_ids, *target_pos, *num_accepted, *bonus_ids, *block_table;
   const void *target_hidden, *h_shared;
@@ -66,6 +67,9 @@ struct RopeOut {
 struct GemvArgs {
   // Y[m, n] = sum_k X[m, k] * W[n, k] for m < M, n < Nout.
   int M, Nout, K;
+  // optional device count of live rows (rows at and past it are padding:
+  // tiles that hold only padding rows are skipped); null: all M rows live
+  const int32_t* m_live;
   AMode amode;
   const void* x;               // Plain
   const int32_t* ids;          // Gather
@@ -105,8 +109,8 @@ bool gemv_uses_mfma(int M, int K, DType dt);
 // ---------------------------------------------------------------- small kernels
 hipError_t launch_build_fc_input(DType dt, int N, int H, const int32_t* ids, const void* embed,
                                  const void* draft_hidden, void* out, hipStream_t s);
-hipError_t launch_rmsnorm(DType dt, int rows, int H, const int32_t* row_idx, const float* x,
-                          const void* gain, float eps, void* out, hipStream_t s);
+hipError_t launch_rmsnorm(DType dt, int rows, int H, const int32_t* row_idx, const float* x, const void* gain,
+                          float eps, void* out, hipStream_t s, const int32_t* live = nullptr);
 
 struct RopeArgs {
   int N, n_q, n_kv, d, block_size;

@@ -8,7 +8,9 @@
 // listing in "P-EAGLE: Faster LLM Inference with Parallel Speculative Decoding
 // in vLLM", vLLM implementation details: target hidden rows move to their new
 // rows and the learned shared hidden state fills the MASK rows.  KV Cache and
-// CUDA Graphs: rejected rows get slot -1.
+// CUDA Graphs: rejected rows get slot -1.  The compacted layout drops the
+// rejected rows instead (a + K rows per sequence) and parks inert padding rows
+// after the live ones, so buffer shapes stay those of the fixed layout.
 //
 // One launch, grid (sequence, column chunk), 256 threads:
 //   * every block derives its sequence's first verified row with a block-wide
@@ -23,12 +25,14 @@
 namespace pe {
 namespace {
 
+// sum of v[0..n) over the block (every thread gets it); callable repeatedly
 __device__ __forceinline__ int block_prefix_sum(const int32_t* v, int n) {
   __shared__ int part[4];
   int s = 0;
   for (int i = threadIdx.x; i < n; i += blockDim.x) s += v[i];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  __syncthreads();
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
   __syncthreads();
   const int total = part[0] + part[1] + part[2] + part[3];
@@ -42,8 +46,18 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepareArgs a, int row_byt
   const int K = a.K;
   const int L = a.query_lens[i];
   const int acc = a.num_accepted[i];
-  const int D = s + i * (K - 1);
-  const int rows = L + K - 1;
+  // fixed layout: L + K - 1 rows per sequence (rejected rows kept, inert);
+  // compacted: a + K rows (rejected rows dropped), then inert padding rows up
+  // to the fixed total, sequence i padding as many rows as it dropped
+  const int D_fixed = s + i * (K - 1);
+  int D = D_fixed, rows = L + K - 1, live = a.N, pad0 = 0, npad = 0;
+  if (a.compact) {
+    D = block_prefix_sum(a.num_accepted, i) + i * K;
+    rows = acc + K;
+    live = block_prefix_sum(a.num_accepted, a.c) + a.c * K;
+    pad0 = live + (D_fixed - D);
+    npad = L - 1 - acc;
+  }
 
   if (blockIdx.y == 0) {
     const int bonus = a.bonus_ids[i];
@@ -74,13 +88,21 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepareArgs a, int row_byt
       a.slot_mapping[row] =
           rejected ? int64_t(-1) : int64_t(bt[pos / bs]) * bs + pos % bs;
     }
+    for (int r = threadIdx.x; r < npad; r += blockDim.x) {
+      const int row = pad0 + r;             // padding: never written, attended or sampled
+      a.draft_ids[row] = bonus;
+      a.draft_pos[row] = 0;
+      a.is_masked[row] = 0;
+      a.is_rejected[row] = 1;
+      a.slot_mapping[row] = int64_t(-1);
+    }
     for (int j = threadIdx.x; j < L; j += blockDim.x)
-      a.hidden_map[s + j] = j <= acc ? D + j : D + j + K - 1;
+      a.hidden_map[s + j] = j <= acc ? D + j : (a.compact ? -1 : D + j + K - 1);
     for (int k = threadIdx.x; k < K; k += blockDim.x) a.sample_idx[i * K + k] = D + acc + k;
     if (threadIdx.x == 0) {
       a.cu_draft[i] = D;
       a.kv_lens[i] = base + K;
-      if (i == a.c - 1) a.cu_draft[a.c] = a.N;
+      if (i == a.c - 1) a.cu_draft[a.c] = live;
     }
   }
 
@@ -103,6 +125,11 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepareArgs a, int row_byt
       src = th + static_cast<int64_t>(s + j) * row_bytes + v * 16;
     }
     store16(out + static_cast<int64_t>(D + r) * row_bytes + v * 16, load16(src));
+  }
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (int f = threadIdx.x; f < npad * width; f += blockDim.x) {
+    const int r = f / width;
+    store16(out + static_cast<int64_t>(pad0 + r) * row_bytes + (v0 + f - r * width) * 16, zero);
   }
 }
 

@@ -26,9 +26,11 @@ __global__ __launch_bounds__(256) void fc_input_kernel(int H_bytes, const int32_
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(int H, const int32_t* __restrict__ row_idx,
                                                       const float* __restrict__ x, const T* __restrict__ gain,
-                                                      float eps, T* __restrict__ out) {
+                                                      float eps, T* __restrict__ out,
+                                                      const int32_t* __restrict__ live) {
   __shared__ float part[4];
   const int i = blockIdx.x;
+  if (live && i >= *live) return;  // padding row of the compacted layout
   const int r = row_idx ? row_idx[i] : i;
   const f32x4* xr = reinterpret_cast<const f32x4*>(x + static_cast<int64_t>(r) * H);
   const int nv = H / 4;
@@ -141,14 +143,14 @@ hipError_t launch_build_fc_input(DType dt, int N, int H, const int32_t* ids, con
 }
 
 hipError_t launch_rmsnorm(DType dt, int rows, int H, const int32_t* row_idx, const float* x, const void* gain,
-                          float eps, void* out, hipStream_t s) {
+                          float eps, void* out, hipStream_t s, const int32_t* live) {
   dim3 grid(rows);
   if (dt == DType::F32)
     hipLaunchKernelGGL(rmsnorm_kernel<float>, grid, dim3(256), 0, s, H, row_idx, x,
-                       static_cast<const float*>(gain), eps, static_cast<float*>(out));
+                       static_cast<const float*>(gain), eps, static_cast<float*>(out), live);
   else
     hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, grid, dim3(256), 0, s, H, row_idx, x,
-                       static_cast<const bf16_t*>(gain), eps, static_cast<bf16_t*>(out));
+                       static_cast<const bf16_t*>(gain), eps, static_cast<bf16_t*>(out), live);
   return hipGetLastError();
 }
 

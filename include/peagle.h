@@ -5,6 +5,7 @@
  * proposes K draft tokens per sequence with a single drafter pass:
  *
  *   pe_prepare_draft_batch  expand the verified batch into the draft layout and
+ *                           (pe_prepare_draft_batch_compact: without rejected rows)
  *                           place the hidden states (target rows moved to their
  *                           new rows, the learned shared hidden state broadcast
  *                           into the MASK rows);
@@ -148,6 +149,26 @@ size_t pe_workspace_bytes(const pe_model *model, int32_t num_seqs, int32_t K, in
  *   draft_hidden[N,H]  placed hidden states
  */
 pe_status pe_prepare_draft_batch(const pe_model *model, int32_t num_seqs, int32_t K,
+                                 int32_t total_target_rows, const int32_t *query_lens,
+                                 const int32_t *target_ids, const int32_t *target_pos,
+                                 const int32_t *num_accepted, const int32_t *bonus_ids,
+                                 const void *target_hidden, const int32_t *block_table,
+                                 int32_t max_blocks, int32_t *draft_ids, int32_t *draft_pos,
+                                 int64_t *slot_mapping, uint8_t *is_rejected, uint8_t *is_masked,
+                                 int32_t *hidden_map, int32_t *cu_draft, int32_t *kv_lens,
+                                 int32_t *sample_idx, void *draft_hidden, hipStream_t stream);
+
+/* Compacted draft layout (the fixed layout keeps rejected rows as inert
+ * slot -1 rows, "P-EAGLE: Parallel Speculative Decoding in vLLM", KV Cache and
+ * CUDA Graphs; this one drops them).  Same arguments and buffer sizes as
+ * pe_prepare_draft_batch (N = T + c(K-1) rows), but sequence i owns only its
+ * a_i + K live rows -- the accepted rows, the bonus row and the K-1 MASK rows
+ * -- at cu_draft[i] = sum_{j<i} (a_j + K).  cu_draft[c] holds the number of
+ * live rows; the rows from there to N are inert padding (slot -1, flagged
+ * rejected, zero hidden state) that pe_draft_forward skips tile by tile.
+ * hidden_map[t] is -1 for target rows past the accepted prefix (no draft row
+ * inherits them).  Tokens and logits equal those of the fixed layout. */
+pe_status pe_prepare_draft_batch_compact(const pe_model *model, int32_t num_seqs, int32_t K,
                                  int32_t total_target_rows, const int32_t *query_lens,
                                  const int32_t *target_ids, const int32_t *target_pos,
                                  const int32_t *num_accepted, const int32_t *bonus_ids,

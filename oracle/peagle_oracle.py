@@ -80,7 +80,7 @@ def round_operand(x64: np.ndarray, dtype: str, precision: str = "mirror") -> np.
 # Step 1: expand the verified batch into the draft layout
 # ----------------------------------------------------------------------------
 def expand_batch(query_lens, target_ids, target_pos, num_accepted, bonus_ids, block_table,
-                 K: int, mask_id: int, block_size: int = 16) -> Dict[str, np.ndarray]:
+                 K: int, mask_id: int, block_size: int = 16, compact: bool = False) -> Dict[str, np.ndarray]:
     """Draft-batch metadata, one row kind at a time.
 
     [PP] "Fused Triton Kernel": in one pass the previous token ids and
@@ -105,6 +105,13 @@ def expand_batch(query_lens, target_ids, target_pos, num_accepted, bonus_ids, bl
         ids and original positions, and get slot -1;
       * the K sampled rows are the NTP row and the MASK rows;
       * the sequence's KV length after the pass is target_pos[s+a_i] + K.
+
+    ``compact``: the rejected rows are dropped instead of kept as slot -1
+    rows, so sequence i owns a_i + K rows from D_i = sum_{j<i} (a_j + K);
+    cu_draft[c] is the number of live rows and the arrays keep the fixed
+    layout's length N, the rows past the live ones being inert padding (slot
+    -1, flagged rejected, id = the sequence's bonus token, position 0); target
+    rows past the accepted prefix map to -1 (no draft row inherits them).
     """
     query_lens = np.asarray(query_lens, dtype=np.int64)
     target_ids = np.asarray(target_ids, dtype=np.int64)
@@ -127,17 +134,27 @@ def expand_batch(query_lens, target_ids, target_pos, num_accepted, bonus_ids, bl
     sample_idx = np.zeros(c * K, np.int64)
 
     s = 0
+    live = int(num_accepted.sum()) + c * K if compact else N
+    pad = live                                  # next padding row (compact)
+    Dc = 0                                      # next live row (compact)
     for i in range(c):
         L = int(query_lens[i])
         a = int(num_accepted[i])
         b = int(bonus_ids[i])
         if not (0 <= a <= L - 1):
             raise ValueError(f"sequence {i}: accepted count {a} outside 0..{L - 1}")
-        D = s + i * (K - 1)
+        D = Dc if compact else s + i * (K - 1)
         cu_draft[i] = D
         base = int(target_pos[s + a])
         kv_lens[i] = base + K
-        for r in range(L + K - 1):
+        if compact:
+            for r in range(L - 1 - a):          # this sequence's share of padding rows
+                ids[pad] = b
+                rej[pad] = 1
+                slot[pad] = PADDING_SLOT_ID
+                pad += 1
+            Dc += a + K
+        for r in range(a + K if compact else L + K - 1):
             row = D + r
             if r <= a:                          # accepted rows, then the bonus (NTP) row
                 ids[row] = target_ids[s + r + 1] if r < a else b
@@ -157,11 +174,11 @@ def expand_batch(query_lens, target_ids, target_pos, num_accepted, bonus_ids, bl
                 p = int(pos[row])
                 slot[row] = block_table[i, p // block_size] * block_size + p % block_size
         for j in range(L):
-            hmap[s + j] = D + j if j <= a else D + j + K - 1
+            hmap[s + j] = D + j if j <= a else (-1 if compact else D + j + K - 1)
         for k in range(K):
             sample_idx[i * K + k] = D + a + k
         s += L
-    cu_draft[c] = N
+    cu_draft[c] = live
     return dict(draft_ids=ids, draft_pos=pos, slot_mapping=slot, is_rejected=rej,
                 is_masked=msk, hidden_map=hmap, cu_draft=cu_draft, kv_lens=kv_lens,
                 sample_idx=sample_idx)
@@ -179,7 +196,8 @@ def scatter_broadcast(target_hidden: np.ndarray, hidden_map, is_masked, h_shared
     target_hidden = np.asarray(target_hidden)
     out = np.zeros((num_rows,) + target_hidden.shape[1:], dtype=target_hidden.dtype)
     for t, r in enumerate(np.asarray(hidden_map)):
-        out[int(r)] = target_hidden[t]
+        if r >= 0:                      # -1: dropped (compacted layout)
+            out[int(r)] = target_hidden[t]
     for r in range(num_rows):
         if is_masked[r]:
             out[r] = h_shared
@@ -477,11 +495,12 @@ def autoregressive_draft(spec, weights: dict, batch, K: int, precision: str = "m
 # whole round
 # ----------------------------------------------------------------------------
 def parallel_draft_step(spec, weights: dict, batch, precision: str = "mirror",
-                        seqs: Optional[Sequence[int]] = None, want_logits: bool = True) -> dict:
+                        seqs: Optional[Sequence[int]] = None, want_logits: bool = True,
+                        compact: bool = False) -> dict:
     """Expand, place hidden states, run the drafter pass (no acceptance)."""
     meta = expand_batch(batch.query_lens, batch.target_ids, batch.target_pos, batch.num_accepted,
                         batch.bonus_ids, batch.block_table, batch.K, spec.mask_token_id,
-                        spec.block_size)
+                        spec.block_size, compact=compact)
     hd = scatter_broadcast(batch.target_hidden, meta["hidden_map"], meta["is_masked"],
                            weights["h_shared"], len(meta["draft_ids"]))
     fwd = draft_forward(spec, weights, meta, hd, batch.block_table, batch.k_cache, batch.v_cache,

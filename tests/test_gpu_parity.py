@@ -197,6 +197,42 @@ def test_forward_without_logits_matches(name):
     assert np.array_equal(gap_a, from_torch(gap_b))
 
 
+@pytest.mark.parametrize("name", ["gptoss20b-bf16-c64-k7", "qwen3coder30b-bf16-c16-k5", "tiny-fp32-c2-k3"])
+def test_compact_layout(name):
+    """Compacted layout (rejected rows dropped): the expansion is bit-exact
+    against the oracle's, and the drafter pass over it returns exactly the
+    fixed layout's tokens, gaps and logits on the same batch."""
+    import drafting_draft_expand_amd as pe
+    wl = synth.WORKLOADS[name]
+    spec = wl.model
+    _say(f"compact layout {wl.name}")
+    w = host_weights(spec, wl.wseed)
+    model = device_model(spec, wl.wseed)
+    b = synth.make_batch(wl)
+    db = upload_batch(b, "cuda:0")
+    meta = oracle.expand_batch(b.query_lens, b.target_ids, b.target_pos, b.num_accepted, b.bonus_ids,
+                               b.block_table, b.K, spec.mask_token_id, spec.block_size, compact=True)
+    hd = oracle.scatter_broadcast(b.target_hidden, meta["hidden_map"], meta["is_masked"], w["h_shared"],
+                                  len(meta["draft_ids"]))
+    outs = {}
+    for compact in (False, True):
+        prep = pe.prepare_draft_batch(model, b.K, db["query_lens"], db["target_ids"], db["target_pos"],
+                                      db["num_accepted"], db["bonus_ids"], db["target_hidden"], db["block_table"],
+                                      compact=compact)
+        logits = torch.empty((wl.c * b.K, spec.vocab), dtype=torch.float32, device="cuda:0")
+        gap = torch.empty(wl.c * b.K, dtype=torch.float32, device="cuda:0")
+        tokens = pe.draft_forward(model, prep, db["block_table"], db["k_cache"], db["v_cache"], logits=logits,
+                                  top2_gap=gap)
+        torch.cuda.synchronize()
+        if compact:
+            check_prepare_exact(prep, meta, hd)
+        outs[compact] = (from_torch(tokens).copy(), from_torch(gap).copy(), from_torch(logits).copy())
+    live = int(meta["cu_draft"][-1])
+    _say(f"  live rows {live} of {len(meta['draft_ids'])}")
+    for a_, b_ in zip(outs[False], outs[True]):
+        assert np.array_equal(a_, b_)
+
+
 # ----------------------------------------------------------------------------- acceptance
 @pytest.mark.parametrize("name", ["tiny-fp32-c2-k3", "qwen3coder30b-bf16-c16-k7"])
 def test_accept_matches_oracle(name):
