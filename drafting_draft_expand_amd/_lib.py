@@ -24,7 +24,7 @@ PE_KERNEL_LM_HEAD, PE_KERNEL_PREPARE, PE_KERNEL_ATTENTION = 0, 1, 2
 EXPORTED = ("pe_model_create", "pe_model_destroy", "pe_workspace_bytes", "pe_prepare_draft_batch",
             "pe_draft_forward", "pe_accept", "pe_status_string", "pe_timing_enable", "pe_timing_read",
             "pe_autoregressive_workspace_bytes", "pe_draft_autoregressive", "pe_next_verified_batch",
-            "pe_prepare_draft_batch_compact")
+            "pe_prepare_draft_batch_compact", "pe_packed_weights_bytes", "pe_model_pack_weights")
 
 
 class PeError(RuntimeError):
@@ -65,6 +65,10 @@ def load() -> ctypes.CDLL:
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.pe_model_create.argtypes = [ctypes.POINTER(ModelDesc), ctypes.POINTER(Weights), ctypes.POINTER(P)]
     lib.pe_model_create.restype = I32
+    lib.pe_packed_weights_bytes.argtypes = [P]
+    lib.pe_packed_weights_bytes.restype = SZ
+    lib.pe_model_pack_weights.argtypes = [P, P, SZ, P]
+    lib.pe_model_pack_weights.restype = I32
     lib.pe_model_destroy.argtypes = [P]
     lib.pe_model_destroy.restype = None
     lib.pe_workspace_bytes.argtypes = [P, I32, I32, I32]
@@ -121,11 +125,13 @@ def _dtype_code(dtype: str) -> int:
 
 
 class DraftModel:
-    """A drafter handle: shape description + borrowed device weights."""
+    """A drafter handle: shape description + borrowed device weights, plus (for
+    bf16 drafters, unless ``pack=False``) the packed copy of the projection
+    weights that pe_model_pack_weights fills."""
 
     def __init__(self, hidden: int, vocab: int, n_layers: int, n_q: int, n_kv: int, head_dim: int,
                  inter: int, dtype: str, weights: Dict, block_size: int = 16, rms_eps: float = 1e-6,
-                 rope_theta: float = 10000.0, mask_token_id: Optional[int] = None):
+                 rope_theta: float = 10000.0, mask_token_id: Optional[int] = None, pack: bool = True):
         lib = load()
         self.dtype = dtype
         self.torch_dtype = torch.float32 if dtype == "fp32" else torch.bfloat16
@@ -144,11 +150,17 @@ class DraftModel:
         _check(lib.pe_model_create(ctypes.byref(self.desc), ctypes.byref(self._w), ctypes.byref(h)),
                "pe_model_create")
         self.handle = h
+        self.packed = None
+        nbytes = int(lib.pe_packed_weights_bytes(h))
+        if pack and nbytes > 0:
+            dev = next(t.device for t in weights.values() if isinstance(t, torch.Tensor))
+            self.packed = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            _check(lib.pe_model_pack_weights(h, _ptr(self.packed), nbytes, _stream(None)), "pe_model_pack_weights")
 
     @classmethod
-    def from_spec(cls, spec, weights: Dict) -> "DraftModel":
+    def from_spec(cls, spec, weights: Dict, pack: bool = True) -> "DraftModel":
         return cls(spec.hidden, spec.vocab, spec.n_layers, spec.n_q, spec.n_kv, spec.head_dim, spec.inter,
-                   spec.dtype, weights, spec.block_size, spec.rms_eps, spec.rope_theta, spec.mask_token_id)
+                   spec.dtype, weights, spec.block_size, spec.rms_eps, spec.rope_theta, spec.mask_token_id, pack)
 
     def workspace_bytes(self, num_seqs: int, K: int, num_rows: int) -> int:
         return int(load().pe_workspace_bytes(self.handle, num_seqs, K, num_rows))

@@ -24,10 +24,18 @@ struct Timing {
 
 }  // namespace
 
+// Packed copies of the projection weights (caller-owned buffer attached by
+// pe_model_pack_weights), read by the weight-streaming MFMA kernel.
+struct PackedLayer {
+  const void *qkv, *o, *gate, *up, *down;
+};
+
 struct pe_model {
   pe_model_desc d;
   pe_weights w;
   std::vector<pe_layer_weights> layers;
+  const void* pk_fc = nullptr;
+  std::vector<PackedLayer> pk_layers;  // empty: not packed
   int num_cus = 0;  // queried on first launch
   pe::RopeFreq freq; // theta^(-2j/d) in double precision
   Timing timing[3];
@@ -53,9 +61,14 @@ int attention_splits(int c, int n_kv) {
 
 // Workspace carve-up for one forward call.
 struct Workspace {
-  size_t x, act, qkv, q, attn_part, mlp, top2, f, ss0, total;
+  size_t x, act, qkv, q, attn_part, mlp, top2, f, ss0, part, total;
   int splits, lm_parts;
 };
+
+// Split partials of the few-row projections that write the residual rows.
+inline size_t part_bytes(const pe_model_desc& d, int N) {
+  return N <= 16 ? size_t(pe::kMaxSplits) * N * d.hidden * 4 : 0;
+}
 
 Workspace plan_workspace(const pe_model* m, int c, int K, int N) {
   const pe_model_desc& d = m->d;
@@ -78,13 +91,14 @@ Workspace plan_workspace(const pe_model* m, int c, int K, int N) {
   w.top2 = off;      off += align_up(size_t(S) * w.lm_parts * sizeof(pe::Top2));
   w.f = off;         off += align_up(size_t(S) * H * eb);
   w.ss0 = off;       off += align_up(size_t((H + 15) / 16) * N * 4);
+  w.part = off;      off += align_up(part_bytes(d, N));
   w.total = off;
   return w;
 }
 
 pe_status check_desc(const pe_model_desc* d) {
   if (!d) return PE_EINVAL;
-  if (d->hidden <= 0 || d->hidden % 8 != 0) return PE_EUNSUPPORTED;
+  if (d->hidden <= 0 || d->hidden % 8 != 0 || d->hidden > pe::kMaxHidden) return PE_EUNSUPPORTED;
   if (d->n_layers < 0 || d->block_size != 16) return PE_EUNSUPPORTED;
   if (d->dtype != PE_F32 && d->dtype != PE_BF16) return PE_EUNSUPPORTED;
   if (d->n_layers == 0) return PE_OK;  // expansion-only model
@@ -215,6 +229,69 @@ void pe_model_destroy(pe_model* m) {
   delete m;
 }
 
+namespace {
+// The matrices the weight-streaming kernel reads, in buffer order: fc, then
+// per layer q/k/v (RoPE pair order), o, gate, up, down.  Empty when the model
+// has no bf16 layers or a dimension the kernel cannot take (K % 32).
+void pack_plan(const pe_model* m, std::vector<pe::PackArgs>& v) {
+  v.clear();
+  const pe_model_desc& d = m->d;
+  const int H = d.hidden, qd = d.n_q * d.head_dim, kvd = d.n_kv * d.head_dim, I = d.inter;
+  if (d.dtype != PE_BF16 || d.n_layers <= 0) return;
+  if (H % 32 != 0 || qd % 32 != 0 || I % 32 != 0 || d.head_dim % 16 != 0) return;
+  auto one = [](const void* w, int nout, int k, int rope_d) {
+    pe::PackArgs p{};
+    p.w_a = p.w_b = p.w_c = w; p.n_a = nout; p.n_b = 0; p.Nout = nout; p.K = k; p.rope_d = rope_d;
+    return p;
+  };
+  v.push_back(one(m->w.w_fc, H, 2 * H, 0));
+  for (int l = 0; l < d.n_layers; ++l) {
+    const pe_layer_weights& L = m->layers[l];
+    pe::PackArgs q{};
+    q.w_a = L.wq; q.w_b = L.wk; q.w_c = L.wv; q.n_a = qd; q.n_b = kvd; q.Nout = qd + 2 * kvd; q.K = H;
+    q.rope_d = d.head_dim;
+    v.push_back(q);
+    v.push_back(one(L.wo, H, qd, 0));
+    v.push_back(one(L.w_gate, I, H, 0));
+    v.push_back(one(L.w_up, I, H, 0));
+    v.push_back(one(L.w_down, H, I, 0));
+  }
+}
+}  // namespace
+
+size_t pe_packed_weights_bytes(const pe_model* m) {
+  if (!m) return 0;
+  size_t total = 0;
+  std::vector<pe::PackArgs> plan;
+  pack_plan(m, plan);
+  for (const pe::PackArgs& p : plan) total += align_up(pe::packed_bytes(p.Nout, p.K));
+  return total;
+}
+
+pe_status pe_model_pack_weights(pe_model* m, void* packed, size_t packed_bytes, hipStream_t stream) {
+  if (!m) return PE_EINVAL;
+  std::vector<pe::PackArgs> plan;
+  pack_plan(m, plan);
+  if (plan.empty()) return PE_OK;
+  if (!packed || (reinterpret_cast<uintptr_t>(packed) % kAlign) != 0) return PE_EINVAL;
+  if (packed_bytes < pe_packed_weights_bytes(m)) return PE_EWORKSPACE;
+  std::vector<const void*> dst;
+  char* b = static_cast<char*>(packed);
+  for (pe::PackArgs& p : plan) {
+    p.dst = b;
+    dst.push_back(b);
+    PE_HIP(pe::launch_pack(p, stream));
+    b += align_up(pe::packed_bytes(p.Nout, p.K));
+  }
+  m->pk_fc = dst[0];
+  m->pk_layers.assign(m->d.n_layers, PackedLayer{});
+  for (int l = 0; l < m->d.n_layers; ++l) {
+    const void* const* q = dst.data() + 1 + 5 * l;
+    m->pk_layers[l] = PackedLayer{q[0], q[1], q[2], q[3], q[4]};
+  }
+  return PE_OK;
+}
+
 size_t pe_workspace_bytes(const pe_model* m, int32_t c, int32_t K, int32_t N) {
   if (!m || c <= 0 || K <= 0 || N <= 0 || m->d.n_layers <= 0) return 0;
   return plan_workspace(m, c, K, N).total;
@@ -322,13 +399,17 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
   pe::Top2* top2 = reinterpret_cast<pe::Top2*>(wb + ws.top2);
   void* f = wb + ws.f;
   float* ss0 = reinterpret_cast<float*>(wb + ws.ss0);
+  float* xpart = part_bytes(d, N) ? reinterpret_cast<float*>(wb + ws.part) : nullptr;
   const int cus = num_cus(m);
 
   const int ss_tiles = (H + 15) / 16;
   // rows at and past cu_draft[c] are padding (compacted layout): skipped
   const int32_t* live = cu_draft + c;
   const bool fused = fused_plan(d, N);
-  const bool fnorm = fused && fused_final_norm(d, N, S);
+  const bool packed = !m->pk_layers.empty();
+  // packed models split the down projection instead (the final RMSNorm adds
+  // its partials for the sampled rows)
+  const bool fnorm = fused && !packed && fused_final_norm(d, N, S);
   // attention and LM head are shared by both plans
   auto attention = [&](int l) -> pe_status {
     pe::AttnArgs at{};
@@ -345,6 +426,24 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
     PE_HIP(pe::launch_gemv(g, e, t, cus, stream));
     return PE_OK;
   };
+  // Split partials left in `part` by the last projection into x; the next
+  // RMSNorm of x completes the rows (adding the residual for AddTo).
+  int pend_splits = 0;
+  bool pend_acc = false;
+  auto into_x = [&](pe::GemvArgs& g, pe::Epi e) -> pe_status {
+    g.part = packed && g.pk_a && !g.ss_out ? xpart : nullptr;
+    pe_status r = proj(g, e);
+    if (r != PE_OK) return r;
+    pend_splits = g.splits > 1 ? g.splits : 0;
+    pend_acc = e == pe::Epi::AddTo;
+    return PE_OK;
+  };
+  auto norm_x = [&](const void* gain) -> pe_status {
+    PE_HIP(pe::launch_rmsnorm(t, N, H, nullptr, x, gain, d.rms_eps, act, stream, live, xpart, pend_splits, N,
+                              pend_acc));
+    pend_splits = 0;
+    return PE_OK;
+  };
   pe_status st;
 
   if (fused) {
@@ -354,19 +453,22 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
       g.M = N; g.m_live = live; g.Nout = H; g.K = 2 * H; g.amode = pe::AMode::Gather;
       g.ids = draft_ids; g.embed = m->w.embed; g.x2 = draft_hidden;
       g.w_a = g.w_b = g.w_c = m->w.w_fc; g.n_a = H; g.n_b = 0;
+      g.pk_a = packed ? m->pk_fc : nullptr;
       g.y = x; g.ldy = H;
-      if ((st = proj(g, pe::Epi::Store)) != PE_OK) return st;
+      if ((st = into_x(g, pe::Epi::Store)) != PE_OK) return st;
     }
     for (int l = 0; l < d.n_layers; ++l) {
       const pe_layer_weights& L = m->layers[l];
-      // RMSNorm as its own pass: forming it inside the projection would make
-      // every workgroup re-read the fp32 rows (twice the operand traffic)
-      PE_HIP(pe::launch_rmsnorm(t, N, H, nullptr, x, L.ln1, d.rms_eps, act, stream, live));
+      const PackedLayer* P = packed ? &m->pk_layers[l] : nullptr;
+      // RMSNorm as its own pass (it also completes split partials): forming it
+      // inside the projection would make every workgroup re-read the fp32 rows
+      if ((st = norm_x(L.ln1)) != PE_OK) return st;
       {
         // q/k/v -> RoPE -> q operand + paged KV write
         pe::GemvArgs g{};
         g.M = N; g.m_live = live; g.Nout = qd + 2 * kvd; g.K = H; g.amode = pe::AMode::Plain; g.x = act;
         g.w_a = L.wq; g.n_a = qd; g.w_b = L.wk; g.n_b = kvd; g.w_c = L.wv;
+        g.pk_a = P ? P->qkv : nullptr;
         g.rope.n_q = d.n_q; g.rope.n_kv = d.n_kv; g.rope.d = d.head_dim; g.rope.block_size = d.block_size;
         g.rope.freq = m->freq; g.rope.pos = draft_pos; g.rope.slot = slot_mapping;
         g.rope.rejected = is_rejected; g.rope.q_out = qrot; g.rope.k_cache = k_cache[l];
@@ -378,14 +480,16 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
         pe::GemvArgs g{};
         g.M = N; g.m_live = live; g.Nout = H; g.K = qd; g.amode = pe::AMode::Plain; g.x = act;
         g.w_a = g.w_b = g.w_c = L.wo; g.n_a = H; g.n_b = 0;
+        g.pk_a = P ? P->o : nullptr;
         g.y = x; g.ldy = H;
-        if ((st = proj(g, pe::Epi::AddTo)) != PE_OK) return st;
+        if ((st = into_x(g, pe::Epi::AddTo)) != PE_OK) return st;
       }
-      PE_HIP(pe::launch_rmsnorm(t, N, H, nullptr, x, L.ln2, d.rms_eps, act, stream, live));
+      if ((st = norm_x(L.ln2)) != PE_OK) return st;
       {
         pe::GemvArgs g{};
         g.M = N; g.m_live = live; g.Nout = d.inter; g.K = H; g.amode = pe::AMode::Plain; g.x = act;
         g.w_a = L.w_gate; g.w_b = L.w_up; g.w_c = L.w_up; g.n_a = d.inter; g.n_b = d.inter;
+        g.pk_a = P ? P->gate : nullptr; g.pk_b = P ? P->up : nullptr;
         g.y_op = mlp; g.ldy = d.inter;
         if ((st = proj(g, pe::Epi::SiluMul)) != PE_OK) return st;
       }
@@ -393,8 +497,9 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
         pe::GemvArgs g{};
         g.M = N; g.m_live = live; g.Nout = H; g.K = d.inter; g.amode = pe::AMode::Plain; g.x = mlp;
         g.w_a = g.w_b = g.w_c = L.w_down; g.n_a = H; g.n_b = 0;
+        g.pk_a = P ? P->down : nullptr;
         g.y = x; g.ldy = H; g.ss_out = fnorm && l == d.n_layers - 1 ? ss0 : nullptr;
-        if ((st = proj(g, pe::Epi::AddTo)) != PE_OK) return st;
+        if ((st = into_x(g, pe::Epi::AddTo)) != PE_OK) return st;
       }
     }
   } else {
@@ -448,7 +553,9 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
       }
     }
   }
-  if (!fnorm) PE_HIP(pe::launch_rmsnorm(t, S, H, sample_idx, x, m->w.ln_f, d.rms_eps, f, stream));
+  if (!fnorm)
+    PE_HIP(pe::launch_rmsnorm(t, S, H, sample_idx, x, m->w.ln_f, d.rms_eps, f, stream, nullptr, xpart,
+                              pend_splits, N, pend_acc));
   // LM head + argmax over the sampled rows
   {
     pe::GemvArgs g{};

@@ -109,6 +109,12 @@ template <> __device__ __forceinline__ float dot16<bf16_t>(u32x4 a, u32x4 b, flo
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
+// Raw buffer resources (gfx9 family): word 3 of the descriptor for untyped
+// dword access; loads at offsets >= num_records return zeros without a memory
+// access.  Cache policy 2 marks a load non-temporal (streamed once).
+constexpr int kBufferDword3 = 0x00020000;
+constexpr int kCachePolicyStream = 2;
+
 __device__ __forceinline__ u32x4 load16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }

@@ -12,20 +12,23 @@
 //   per-lane partial sums are folded across the wave with a reduce-scatter, so
 //   every lane ends with one finished dot product and applies the epilogue.
 //
-// mfma_skinny_kernel (bf16, 8 < M <= 16 per slice):
+// mfma_skinny_kernel (bf16, 8 < M <= 16):
 //   at 14-16 rows the VALU would be near saturation at full HBM rate, so the
 //   products run on v_mfma_f32_16x16x32_bf16: the activation rows are the A
 //   operand (one 16-byte piece per lane per k-step) and 16 weight rows are the
-//   B operand, loaded straight from HBM in the MFMA lane layout.  The SK waves
-//   of a workgroup split K, their partial tiles are summed through LDS and
-//   wave 0 applies the epilogue.
+//   B operand.  The weights come from a packed copy in MFMA fragment order
+//   (each wave load one contiguous KiB) or, for the LM head and unpacked
+//   models, straight from row-major W.  A workgroup owns 1, 2 or 4 column
+//   tiles (one A fragment feeds all of them) and one of `splits` ranges of K;
+//   its waves split that range again and meet in LDS.
 //
 // The activation operand can be formed on the fly (AMode): the fc input
 // concatenation [emb(id) ; h], or RMSNorm of fp32 residual rows whose sums of
 // squares arrive as per-tile partials from the kernel that produced them
-// (Store/AddTo epilogues emit them), so no separate normalisation launch is
-// needed.  Epilogues: store, residual add, SiLU(gate)*up, LM-head argmax
-// candidates, and q/k/v with RoPE and the paged KV write.
+// (Store/AddTo epilogues emit them) for the LM head.  Epilogues: store,
+// residual add (or split partials that the next RMSNorm adds up),
+// SiLU(gate)*up, LM-head argmax candidates, and q/k/v with RoPE and the paged
+// KV write.
 #include "common.h"
 
 namespace pe {
@@ -80,7 +83,7 @@ __device__ __forceinline__ u32x4 load_a16(const GemvArgs& a, int m, int kv, floa
 }
 
 // ------------------------------------------------------------------ VALU / LDS
-template <typename TW, int MT, int R, Epi EPI, AMode MODE>
+template <typename TW, int MT, int R, Epi EPI, AMode MODE, int JS = 2>
 __global__ __launch_bounds__(256) void gemv_lds_kernel(GemvArgs a) {
   constexpr int VE = Elem<TW>::kVec;
   constexpr int NV = R * MT;
@@ -139,22 +142,22 @@ __global__ __launch_bounds__(256) void gemv_lds_kernel(GemvArgs a) {
     float acc[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) acc[i] = 0.f;
-    for (int j = lane; j < KV; j += 128) {
-      const bool two = j + 64 < KV;
+    // JS 64-lane k-steps of all R rows are requested before any is used
+    for (int j = lane; j < KV; j += 64 * JS) {
       const u32x4 zero = {0u, 0u, 0u, 0u};
-      u32x4 w0[R], w1[R];
+      u32x4 wv[JS][R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) w0[r] = load16_stream(wp[r] + j * VE);
+      for (int js = 0; js < JS; ++js)
 #pragma unroll
-      for (int r = 0; r < R; ++r) w1[r] = two ? load16_stream(wp[r] + (j + 64) * VE) : zero;
+        for (int r = 0; r < R; ++r)
+          wv[js][r] = (js == 0 || j + 64 * js < KV) ? load16_stream(wp[r] + (j + 64 * js) * VE) : zero;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const u32x4 x0 = xs[m * KV + j];
-        const u32x4 x1 = two ? xs[m * KV + j + 64] : zero;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          acc[r * MT + m] = dot16<TW>(w0[r], x0, acc[r * MT + m]);
-          acc[r * MT + m] = dot16<TW>(w1[r], x1, acc[r * MT + m]);
+        for (int js = 0; js < JS; ++js) {
+          const u32x4 xv = (js == 0 || j + 64 * js < KV) ? xs[m * KV + j + 64 * js] : zero;
+#pragma unroll
+          for (int r = 0; r < R; ++r) acc[r * MT + m] = dot16<TW>(wv[js][r], xv, acc[r * MT + m]);
         }
       }
     }
@@ -204,41 +207,67 @@ __global__ __launch_bounds__(256) void gemv_lds_kernel(GemvArgs a) {
 }
 
 // ------------------------------------------------------------------ MFMA skinny
-// Row of W feeding column c (0..15) of tile t.  For QkvRope a tile holds 8
-// rotary pairs of one head: columns c and c+8 are elements j and j + d/2.
+// Row of W feeding column c (0..15) of tile t.  For the q/k/v projection a tile
+// holds 8 rotary pairs of one head: columns c and c+8 are elements j and j + d/2.
+__device__ __forceinline__ int rope_tile_row(int t, int c, int d) {
+  const int per_head = d / 16;
+  const int head = t / per_head, p = t - head * per_head;
+  return head * d + 8 * p + (c & 7) + (c >= 8 ? d / 2 : 0);
+}
 template <Epi EPI>
 __device__ __forceinline__ int tile_row(const GemvArgs& a, int t, int c) {
-  if constexpr (EPI == Epi::QkvRope) {
-    const int per_head = a.rope.d / 16;
-    const int head = t / per_head, p = t - head * per_head;
-    return head * a.rope.d + 8 * p + (c & 7) + (c >= 8 ? a.rope.d / 2 : 0);
-  } else {
-    return t * 16 + c;
-  }
+  if constexpr (EPI == Epi::QkvRope) return rope_tile_row(t, c, a.rope.d);
+  else return t * 16 + c;
 }
 
-template <int SK, int U, Epi EPI, AMode MODE>
+// Weight-streaming MFMA projection of at most 16 activation rows.
+//
+// Grid (groups, splits).  Workgroup (g, z) owns the NT 16-column tiles
+// [g NT, g NT + NT) (grid-stride over groups) and the z-th of `splits` equal
+// ranges of k-steps (32 elements each); its SK waves divide that range again.
+// Per k-step a wave loads one A fragment (activation rows, one 16-byte piece
+// per lane) and NT * NB B fragments, so the activation traffic is 1 / (NT NB)
+// of the weight traffic.  B fragments come either from the packed copy, where
+// fragment (t, s) is one contiguous KiB and a wave's load is fully coalesced,
+// or straight from row-major W (64 bytes of each of 16 rows).
+//
+// The steady state is branch-free.  Packed B fragments are read through a
+// buffer resource per wave and tile that spans exactly the wave's fragments, so
+// k-steps past the range (and tiles past the end) read zeros without touching
+// memory; row-major B and the A fragments clamp such steps to the last valid
+// one (A is then zeroed), and tiles past the end to the last tile (their
+// columns are dropped by the epilogue).
+// The SK partial tiles meet in LDS and wave n finishes tile n of the group.
+// With splits > 1 (Store / AddTo only) the finished sums go to part[z] and the
+// consumer adds the splits (and the residual for AddTo) in a fixed order.
+template <int SK, int NT, int U, Epi EPI, AMode MODE, bool PACKED>
 __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
-  constexpr int NB = EPI == Epi::SiluMul ? 2 : 1;  // B tiles per output tile (gate, up)
-  __shared__ f32x4 red[SK][NB][64];
+  static_assert(NT <= SK, "one finishing wave per tile");
+  static_assert(EPI != Epi::Argmax || NT == 1, "argmax candidates are kept by wave 0");
+  constexpr int NB = EPI == Epi::SiluMul ? 2 : 1;  // B fragments per tile (gate, up)
+  constexpr int WSTEP = 32;                          // row-major: elements between k-steps of a lane's B stream
+  __shared__ f32x4 red[SK][NT * NB][64];
   __shared__ float inv_s[16];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int K = a.K;
   const int KS = K / 32;
-  const int per = (KS + SK - 1) / SK;
-  const int ks0 = min(KS, wave * per);
-  const int ks1 = min(KS, ks0 + per);
-  const int m0 = blockIdx.y * 16;
-  if (a.m_live && m0 >= *a.m_live) return;  // only padding rows in this slice
-  const int mrow = m0 + (lane & 15);
+  const int splits = gridDim.y, z = blockIdx.y;
+  const int per_z = (KS + splits - 1) / splits;
+  const int kz0 = min(KS, z * per_z), kz1 = min(KS, kz0 + per_z);
+  const int per = (kz1 - kz0 + SK - 1) / SK;
+  const int ks0 = min(kz1, kz0 + wave * per);
+  const int ks1 = min(kz1, ks0 + per);
+  const int slast = max(ks0, ks1 - 1);             // clamp target (never read when ks0 == ks1)
+  if (a.m_live && *a.m_live <= 0) return;          // only padding rows
+  const int mrow = lane & 15;
   const bool xvalid = mrow < a.M;
   const int mclamp = min(mrow, a.M - 1);
   const int j = lane >> 4;
   if constexpr (MODE == AMode::Norm) {
     for (int m = wave; m < 16; m += SK) {
-      if (m0 + m < a.M) {
-        const int r = a.rows ? a.rows[m0 + m] : m0 + m;
+      if (m < a.M) {
+        const int r = a.rows ? a.rows[m] : m;
         const float inv = inv_rms_of(a, r, lane, 64);
         if (lane == 0) inv_s[m] = inv;
       }
@@ -247,16 +276,16 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
   }
   const float inv = (MODE == AMode::Norm && xvalid) ? inv_s[lane & 15] : 0.f;
   const int T = (a.Nout + 15) / 16;
+  const int G = (T + NT - 1) / NT;
   // q/k/v epilogue: the position, rejected flag and cache slot of this lane's
-  // four output rows are read once, before the weights stream, instead of
-  // after the K loop on every tile (they would be serialised behind the stores)
+  // four output rows are read once, before the weights stream
   int r_pos[4] = {0, 0, 0, 0};
   int64_t r_slot[4] = {-1, -1, -1, -1};
   bool r_live[4] = {false, false, false, false};
   if constexpr (EPI == Epi::QkvRope) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int m = m0 + 4 * j + q;
+      const int m = 4 * j + q;
       if (m < a.M) {
         r_live[q] = !a.rope.rejected[m];
         r_pos[q] = a.rope.pos[m];
@@ -269,86 +298,137 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) best[q] = top2_empty();
 
-  for (int t = blockIdx.x; t < T; t += gridDim.x) {
-    const int nrow = min(tile_row<EPI>(a, t, lane & 15), a.Nout - 1);
-    const bf16_t* wp[NB];
-    if constexpr (EPI == Epi::SiluMul) {
-      wp[0] = static_cast<const bf16_t*>(a.w_a) + static_cast<int64_t>(nrow) * K + j * 8;
-      wp[NB - 1] = static_cast<const bf16_t*>(a.w_b) + static_cast<int64_t>(nrow) * K + j * 8;
-    } else {
-      const bf16_t* base;
-      int rr;
-      if (nrow < a.n_a) {
-        base = static_cast<const bf16_t*>(a.w_a);
-        rr = nrow;
-      } else if (nrow < a.n_a + a.n_b) {
-        base = static_cast<const bf16_t*>(a.w_b);
-        rr = nrow - a.n_a;
-      } else {
-        base = static_cast<const bf16_t*>(a.w_c);
-        rr = nrow - a.n_a - a.n_b;
-      }
-      wp[0] = base + static_cast<int64_t>(rr) * K + j * 8;
-    }
-    f32x4 acc[NB];
+  for (int g = blockIdx.x; g < G; g += gridDim.x) {
+    const bf16_t* wp[NT][NB];
+    __amdgpu_buffer_rsrc_t rs[NT][NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NT; ++n) {
+      const int t = min(g * NT + n, T - 1);
+      if constexpr (PACKED) {
+        // fragments (t, ks0 .. ks1) of this wave; none for tiles past the end
+        const int bytes = g * NT + n < T ? (ks1 - ks0) * 1024 : 0;
+        const int64_t first = (static_cast<int64_t>(t) * KS + ks0) * 512;
+        rs[n][0] = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16_t*>(static_cast<const bf16_t*>(a.pk_a) + first), 0, bytes, kBufferDword3);
+        if constexpr (NB == 2)
+          rs[n][NB - 1] = __builtin_amdgcn_make_buffer_rsrc(
+              const_cast<bf16_t*>(static_cast<const bf16_t*>(a.pk_b) + first), 0, bytes, kBufferDword3);
+      } else {
+        const int nrow = min(tile_row<EPI>(a, t, lane & 15), a.Nout - 1);
+        if constexpr (EPI == Epi::SiluMul) {
+          wp[n][0] = static_cast<const bf16_t*>(a.w_a) + static_cast<int64_t>(nrow) * K + j * 8;
+          wp[n][NB - 1] = static_cast<const bf16_t*>(a.w_b) + static_cast<int64_t>(nrow) * K + j * 8;
+        } else {
+          const bf16_t* base;
+          int rr;
+          if (nrow < a.n_a) {
+            base = static_cast<const bf16_t*>(a.w_a);
+            rr = nrow;
+          } else if (nrow < a.n_a + a.n_b) {
+            base = static_cast<const bf16_t*>(a.w_b);
+            rr = nrow - a.n_a;
+          } else {
+            base = static_cast<const bf16_t*>(a.w_c);
+            rr = nrow - a.n_a - a.n_b;
+          }
+          wp[n][0] = base + static_cast<int64_t>(rr) * K + j * 8;
+        }
+      }
+    }
+    f32x4 acc[NT][NB];
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[n][b] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int s = ks0; s < ks1; s += U) {
-      u32x4 av[U], bv[U][NB];
+      // Issue order: the A fragments (cache hits) first, then the B fragments
+      // step by step, all before the first product; the barrier keeps the
+      // scheduler from sinking loads below products, so the products of step
+      // u wait only for the loads of steps <= u.
+      u32x4 av[U], bv[U][NT][NB];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const bool ok = s + u < ks1;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) bv[u][b] = ok ? load16(wp[b] + (s + u) * 32) : zero;
-        av[u] = (ok && xvalid) ? load_a16<bf16_t, MODE>(a, mclamp, 4 * (s + u) + j, inv) : zero;
+        const int ss = min(s + u, slast);
+        const u32x4 x = load_a16<bf16_t, MODE>(a, mclamp, 4 * ss + j, inv);
+        av[u] = (s + u < ks1 && xvalid) ? x : zero;
       }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int ss = min(s + u, slast);
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            if constexpr (PACKED)
+              bv[u][n][b] = __builtin_amdgcn_raw_buffer_load_b128(rs[n][b], (s + u - ks0) * 1024 + lane * 16, 0,
+                                                                  kCachePolicyStream);
+            else
+              bv[u][n][b] = load16_stream(wp[n][b] + static_cast<int64_t>(ss) * WSTEP);
+          }
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u]),
-                                                           __builtin_bit_cast(bf16x8, bv[u][b]), acc[b], 0, 0, 0);
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            acc[n][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u]),
+                                                                __builtin_bit_cast(bf16x8, bv[u][n][b]), acc[n][b],
+                                                                0, 0, 0);
     }
 #pragma unroll
-    for (int b = 0; b < NB; ++b) red[wave][b][lane] = acc[b];
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) red[wave][n * NB + b][lane] = acc[n][b];
     __syncthreads();
-    if (wave == 0) {
+    const int t = g * NT + wave;
+    if (wave < NT && t < T) {
       f32x4 sum[NB];
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        sum[b] = red[0][b][lane];
+        sum[b] = red[0][wave * NB + b][lane];
 #pragma unroll
-        for (int w = 1; w < SK; ++w) sum[b] += red[w][b][lane];
+        for (int w = 1; w < SK; ++w) sum[b] += red[w][wave * NB + b][lane];
       }
       const int c = lane & 15;
       const int n = tile_row<EPI>(a, t, c);
       if constexpr (EPI == Epi::Store || EPI == Epi::AddTo) {
-        float sq[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int m = m0 + 4 * j + q;
-          float v = sum[0][q];
-          sq[q] = 0.f;
-          if (m < a.M && n < a.Nout) {
-            float* y = a.y + static_cast<int64_t>(m) * a.ldy + n;
-            if constexpr (EPI == Epi::AddTo) v += *y;
-            *y = v;
-            sq[q] = v * v;
-          }
-        }
-        if (a.ss_out) {
+        if (splits > 1) {
+          float* pz = a.part + static_cast<int64_t>(z) * a.M * a.ldy;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
+            const int m = 4 * j + q;
+            if (m < a.M && n < a.Nout) pz[static_cast<int64_t>(m) * a.ldy + n] = sum[0][q];
+          }
+        } else {
+          float sq[4];
 #pragma unroll
-            for (int off = 8; off >= 1; off >>= 1) sq[q] += __shfl_xor(sq[q], off, 64);
-            const int m = m0 + 4 * j + q;
-            if (c == 0 && m < a.M) a.ss_out[static_cast<int64_t>(t) * a.M + m] = sq[q];
+          for (int q = 0; q < 4; ++q) {
+            const int m = 4 * j + q;
+            float v = sum[0][q];
+            sq[q] = 0.f;
+            if (m < a.M && n < a.Nout) {
+              float* y = a.y + static_cast<int64_t>(m) * a.ldy + n;
+              if constexpr (EPI == Epi::AddTo) v += *y;
+              *y = v;
+              sq[q] = v * v;
+            }
+          }
+          if (a.ss_out) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+              for (int off = 8; off >= 1; off >>= 1) sq[q] += __shfl_xor(sq[q], off, 64);
+              const int m = 4 * j + q;
+              if (c == 0 && m < a.M) a.ss_out[static_cast<int64_t>(t) * a.M + m] = sq[q];
+            }
           }
         }
       } else if constexpr (EPI == Epi::SiluMul) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int m = m0 + 4 * j + q;
+          const int m = 4 * j + q;
           if (m >= a.M || n >= a.Nout) continue;
           const float v = sum[0][q];
           const float sg = v / (1.f + expf(-v));
@@ -357,7 +437,7 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
       } else if constexpr (EPI == Epi::Argmax) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int m = m0 + 4 * j + q;
+          const int m = 4 * j + q;
           if (m >= a.M || n >= a.Nout) continue;
           const float v = sum[0][q];
           if (a.logits) a.logits[static_cast<int64_t>(m) * a.Nout + n] = v;
@@ -373,7 +453,7 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
         const double inv_freq = ro.freq.inv[jj];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int m = m0 + 4 * j + q;
+          const int m = 4 * j + q;
           const float v = sum[0][q];
           const float partner = __shfl_xor(v, 8, 64);
           if (!r_live[q]) continue;
@@ -389,11 +469,11 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
             const int64_t slot = r_slot[q];
             if (slot < 0) continue;
             const bool is_k = head < ro.n_q + ro.n_kv;
-            const int g = is_k ? head - ro.n_q : head - ro.n_q - ro.n_kv;
+            const int gg = is_k ? head - ro.n_q : head - ro.n_q - ro.n_kv;
             // 16-token pages (the only page size the library accepts)
             const int64_t blk = slot >> 4;
             const int off = static_cast<int>(slot & 15);
-            static_cast<bf16_t*>(is_k ? ro.k_cache : ro.v_cache)[((blk * ro.n_kv + g) * 16 + off) * d + e] =
+            static_cast<bf16_t*>(is_k ? ro.k_cache : ro.v_cache)[((blk * ro.n_kv + gg) * 16 + off) * d + e] =
                 f32_to_bf16(out);
           }
         }
@@ -415,11 +495,38 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
           o.pad = 0;
           best[q] = top2_merge(best[q], o);
         }
-        const int m = m0 + 4 * j + q;
+        const int m = 4 * j + q;
         if ((lane & 15) == 0 && m < a.M) a.partials[static_cast<int64_t>(m) * gridDim.x + blockIdx.x] = best[q];
       }
     }
   }
+}
+
+// Packed copy: fragment (t, s) of W is 64 16-byte pieces, piece l holding
+// W[row(t, l % 16)][32 s + 8 (l / 16) .. + 8] (zeros past the last row).
+__global__ __launch_bounds__(256) void pack_kernel(PackArgs p) {
+  const int64_t piece = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int KS = p.K / 32;
+  const int64_t pieces = static_cast<int64_t>((p.Nout + 15) / 16) * KS * 64;
+  if (piece >= pieces) return;
+  const int lane = static_cast<int>(piece & 63);
+  const int64_t frag = piece >> 6;
+  const int t = static_cast<int>(frag / KS);
+  const int s = static_cast<int>(frag - static_cast<int64_t>(t) * KS);
+  const int c = lane & 15;
+  const int row = p.rope_d > 0 ? rope_tile_row(t, c, p.rope_d) : t * 16 + c;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (row < p.Nout) {
+    const bf16_t* src;
+    if (row < p.n_a)
+      src = static_cast<const bf16_t*>(p.w_a) + static_cast<int64_t>(row) * p.K;
+    else if (row < p.n_a + p.n_b)
+      src = static_cast<const bf16_t*>(p.w_b) + static_cast<int64_t>(row - p.n_a) * p.K;
+    else
+      src = static_cast<const bf16_t*>(p.w_c) + static_cast<int64_t>(row - p.n_a - p.n_b) * p.K;
+    v = load16(src + s * 32 + (lane >> 4) * 8);
+  }
+  store16(static_cast<bf16_t*>(p.dst) + piece * 8, v);
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -427,47 +534,108 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
 // 16-row slices beyond that.
 int gemv_m_tile(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
 
-bool use_mfma(int M, int K, DType dt) { return dt == DType::BF16 && M > 8 && K % 32 == 0; }
+bool use_mfma(int M, int K, DType dt) { return dt == DType::BF16 && M > 8 && M <= 16 && K % 32 == 0; }
 
-// Waves per workgroup for the MFMA kernel: enough that each wave's share of
-// K fits in one batch of U_SKINNY k-steps (all its loads in flight at once).
-// Paired gate/up tiles, the argmax state and the RoPE epilogue need more
-// registers: at most 8 waves there.
-constexpr int U_SKINNY = 12;
-int skinny_sk(int K, Epi epi) {
-  const int ks = K / 32;
-  const int sk = ks <= 4 * U_SKINNY ? 4 : ks <= 8 * U_SKINNY ? 8 : 16;
-  return (epi == Epi::Store || epi == Epi::AddTo) ? sk : (sk > 8 ? 8 : sk);
+// Launch shape of the weight-streaming MFMA kernel.
+//   * Row-major weights, or epilogues that need whole sums in one workgroup
+//     with few tiles: one tile per wave group, SK waves enough that each
+//     wave's share of K is one batch of 12 k-steps (at most 8 waves for the
+//     paired gate/up tiles, the argmax state and the RoPE epilogue).
+//   * Packed weights with >= 320 tiles: two tiles per workgroup.
+//   * Packed Store / AddTo whose consumer adds split partials: four tiles per
+//     workgroup and K split over enough workgroups to cover most of the CUs.
+struct SkinnyCfg {
+  int sk, nt, u, splits;
+};
+SkinnyCfg skinny_cfg(const GemvArgs& a, Epi epi, int num_cus) {
+  const int ks = a.K / 32;
+  const int T = (a.Nout + 15) / 16;
+  const bool packed = a.pk_a != nullptr && epi != Epi::Argmax;
+  const bool whole = epi == Epi::Store || epi == Epi::AddTo;
+  if (packed && whole && a.part && !a.ss_out) {
+    // enough splits that each wave's share is one batch of 6 k-steps, and at
+    // least enough workgroups for three quarters of the CUs
+    const int groups = (T + 3) / 4;
+    int sp = (ks + 8 * 6 - 1) / (8 * 6);
+    const int fill = (num_cus * 3 / 4) / groups;
+    if (sp < fill) sp = fill;
+    const int max_sp = ks / 8;  // at least one k-step per wave
+    if (sp > max_sp) sp = max_sp;
+    if (sp > kMaxSplits) sp = kMaxSplits;
+    if (sp >= 2) return {8, 4, 6, sp};
+  }
+  if (packed && T >= 320 && ks >= 16) {
+    // the paired gate/up tiles and the RoPE epilogue need 8-wave register
+    // budgets; q/k/v keeps 12 k-steps per batch
+    if (epi == Epi::SiluMul) return {8, 2, 6, 1};
+    if (epi == Epi::QkvRope) return {8, 2, 12, 1};
+    return {16, 2, 6, 1};
+  }
+  int sk = ks <= 48 ? 4 : ks <= 96 ? 8 : 16;
+  if (!whole && sk > 8) sk = 8;
+  return {sk, 1, 12, 1};
+}
+
+template <int SK, int NT, int U, Epi EPI, AMode MODE, bool PACKED>
+hipError_t launch_skinny_t(GemvArgs& a, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((mfma_skinny_kernel<SK, NT, U, EPI, MODE, PACKED>), grid, dim3(64 * SK), 0, s, a);
+  return hipGetLastError();
 }
 
 template <Epi EPI, AMode MODE>
 hipError_t launch_mfma(GemvArgs& a, int num_cus, hipStream_t s) {
+  const SkinnyCfg cfg = skinny_cfg(a, EPI, num_cus);
   const int T = (a.Nout + 15) / 16;
-  const int gx = T < num_cus * 4 ? T : num_cus * 4;
+  const int G = (T + cfg.nt - 1) / cfg.nt;
+  const int gx = G < num_cus * 4 ? G : num_cus * 4;
   a.grid_x = gx;
-  dim3 grid(gx, (a.M + 15) / 16);
-  switch (skinny_sk(a.K, EPI)) {
-    case 16:
-      if constexpr (EPI == Epi::Store || EPI == Epi::AddTo)
-        hipLaunchKernelGGL((mfma_skinny_kernel<16, U_SKINNY, EPI, MODE>), grid, dim3(1024), 0, s, a);
-      break;
-    case 8: hipLaunchKernelGGL((mfma_skinny_kernel<8, U_SKINNY, EPI, MODE>), grid, dim3(512), 0, s, a); break;
-    default: hipLaunchKernelGGL((mfma_skinny_kernel<4, U_SKINNY, EPI, MODE>), grid, dim3(256), 0, s, a); break;
+  a.splits = cfg.splits;
+  dim3 grid(gx, cfg.splits);
+  constexpr bool rowmajor_only = EPI == Epi::Argmax;
+  if (a.pk_a && !rowmajor_only) {
+    if (cfg.nt == 4) {
+      if constexpr (EPI == Epi::Store || EPI == Epi::AddTo) return launch_skinny_t<8, 4, 6, EPI, MODE, true>(a, grid, s);
+      return hipErrorInvalidValue;
+    }
+    if (cfg.nt == 2) {
+      if constexpr (EPI == Epi::SiluMul)
+        return launch_skinny_t<8, 2, 6, EPI, MODE, true>(a, grid, s);
+      else if constexpr (EPI == Epi::QkvRope)
+        return launch_skinny_t<8, 2, 12, EPI, MODE, true>(a, grid, s);
+      else if constexpr (EPI != Epi::Argmax) return launch_skinny_t<16, 2, 6, EPI, MODE, true>(a, grid, s);
+      return hipErrorInvalidValue;
+    }
+    if constexpr (!rowmajor_only) {
+      switch (cfg.sk) {
+        case 16:
+          if constexpr (EPI == Epi::Store || EPI == Epi::AddTo)
+            return launch_skinny_t<16, 1, 12, EPI, MODE, true>(a, grid, s);
+          return hipErrorInvalidValue;
+        case 8: return launch_skinny_t<8, 1, 12, EPI, MODE, true>(a, grid, s);
+        default: return launch_skinny_t<4, 1, 12, EPI, MODE, true>(a, grid, s);
+      }
+    }
   }
-  return hipGetLastError();
+  switch (cfg.sk) {
+    case 16:
+      if constexpr (EPI == Epi::Store || EPI == Epi::AddTo) return launch_skinny_t<16, 1, 12, EPI, MODE, false>(a, grid, s);
+      return hipErrorInvalidValue;
+    case 8: return launch_skinny_t<8, 1, 12, EPI, MODE, false>(a, grid, s);
+    default: return launch_skinny_t<4, 1, 12, EPI, MODE, false>(a, grid, s);
+  }
 }
 
-template <typename TW, int MT, int R, Epi EPI, AMode MODE>
+template <typename TW, int MT, int R, Epi EPI, AMode MODE, int JS = 2>
 hipError_t launch_lds(GemvArgs& a, dim3 grid, hipStream_t s) {
   const size_t lds = static_cast<size_t>(MT) * a.K * sizeof(TW);
   static bool raised = false;
   if (lds > 64 * 1024 && !raised) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_lds_kernel<TW, MT, R, EPI, MODE>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_lds_kernel<TW, MT, R, EPI, MODE, JS>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
       return hipErrorInvalidValue;
     raised = true;
   }
-  hipLaunchKernelGGL((gemv_lds_kernel<TW, MT, R, EPI, MODE>), grid, dim3(256), lds, s, a);
+  hipLaunchKernelGGL((gemv_lds_kernel<TW, MT, R, EPI, MODE, JS>), grid, dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
@@ -484,7 +652,10 @@ hipError_t launch_valu(GemvArgs& a, int num_cus, hipStream_t s) {
   dim3 grid(gx, (a.M + m_tile - 1) / m_tile);
   switch (m_tile) {
     case 16: return launch_lds<TW, 16, 4, EPI, MODE>(a, grid, s);
-    case 8: return launch_lds<TW, 8, 8, EPI, MODE>(a, grid, s);
+    // one k-step of the 8 weight rows in flight keeps this tile near 150
+    // VGPRs (three waves per SIMD), which streams faster than two steps at
+    // ~235 VGPRs and two waves per SIMD
+    case 8: return launch_lds<TW, 8, 8, EPI, MODE, 1>(a, grid, s);
     case 4: return launch_lds<TW, 4, 16, EPI, MODE>(a, grid, s);
     case 2: return launch_lds<TW, 2, 16, EPI, MODE>(a, grid, s);
     default: return launch_lds<TW, 1, 16, EPI, MODE>(a, grid, s);
@@ -504,6 +675,7 @@ bool gemv_uses_mfma(int M, int K, DType dt) { return proj_kernel(M, K, dt) != Pr
 int gemv_grid_x(int M, int Nout, Epi epi, DType dt, int num_cus, int K) {
   if (proj_kernel(M, K, dt) == ProjKernel::Tiled) return gemm_parts(M, Nout, num_cus);
   if (use_mfma(M, K, dt)) {
+    // the argmax epilogue always runs one tile per group on row-major weights
     const int T = (Nout + 15) / 16;
     return T < num_cus * 4 ? T : num_cus * 4;
   }
@@ -522,9 +694,10 @@ size_t gemv_lds_bytes(int M, int K, DType dt) {
 
 // Supported (epilogue, operand) pairs: every epilogue with a plain operand on
 // the MFMA kernel (QkvRope only there), every epilogue but QkvRope with a plain
-// operand on the LDS kernel; the fused forms Store+Gather (fc), QkvRope+Norm,
-// SiluMul+Norm and Argmax+Norm on the MFMA kernel, Argmax+Norm on the LDS kernel.
+// operand on the LDS kernel; the fused forms Store+Gather (fc) and Argmax+Norm
+// on the MFMA kernel, Argmax+Norm on the LDS kernel.
 hipError_t launch_gemv(GemvArgs& a, Epi epi, DType dt, int num_cus, hipStream_t s) {
+  a.splits = 1;
   if (proj_kernel(a.M, a.K, dt) == ProjKernel::Tiled) return launch_gemm(a, epi, num_cus, s);
   if (use_mfma(a.M, a.K, dt)) {
     if (a.amode == AMode::Plain) {
@@ -538,14 +711,7 @@ hipError_t launch_gemv(GemvArgs& a, Epi epi, DType dt, int num_cus, hipStream_t 
       return hipErrorInvalidValue;
     }
     if (a.amode == AMode::Gather && epi == Epi::Store) return launch_mfma<Epi::Store, AMode::Gather>(a, num_cus, s);
-    if (a.amode == AMode::Norm) {
-      switch (epi) {
-        case Epi::QkvRope: return launch_mfma<Epi::QkvRope, AMode::Norm>(a, num_cus, s);
-        case Epi::SiluMul: return launch_mfma<Epi::SiluMul, AMode::Norm>(a, num_cus, s);
-        case Epi::Argmax: return launch_mfma<Epi::Argmax, AMode::Norm>(a, num_cus, s);
-        default: return hipErrorInvalidValue;
-      }
-    }
+    if (a.amode == AMode::Norm && epi == Epi::Argmax) return launch_mfma<Epi::Argmax, AMode::Norm>(a, num_cus, s);
     return hipErrorInvalidValue;
   }
   if (a.amode == AMode::Plain) {
@@ -569,6 +735,17 @@ hipError_t launch_gemv(GemvArgs& a, Epi epi, DType dt, int num_cus, hipStream_t 
     return dt == DType::F32 ? launch_valu<float, Epi::Argmax, AMode::Norm>(a, num_cus, s)
                             : launch_valu<bf16_t, Epi::Argmax, AMode::Norm>(a, num_cus, s);
   return hipErrorInvalidValue;
+}
+
+size_t packed_bytes(int Nout, int K) { return static_cast<size_t>((Nout + 15) / 16) * 16 * K * 2; }
+
+hipError_t launch_pack(const PackArgs& p, hipStream_t s) {
+  if (p.K % 32 != 0 || p.Nout <= 0) return hipErrorInvalidValue;
+  const int64_t pieces = static_cast<int64_t>((p.Nout + 15) / 16) * (p.K / 32) * 64;
+  const int64_t blocks = (pieces + 255) / 256;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 }  // namespace pe

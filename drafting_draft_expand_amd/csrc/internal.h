@@ -85,16 +85,26 @@ struct GemvArgs {
   // up projection (both Nout rows).
   const void *w_a, *w_b, *w_c;
   int n_a, n_b;
+  // packed copies of the same rows in MFMA fragment order (PackArgs), used by
+  // the weight-streaming MFMA kernel when set: pk_a for all Nout rows (the gate
+  // for SiluMul), pk_b the up projection
+  const void *pk_a, *pk_b;
   // outputs
   float* y;                    // Store / AddTo: fp32 [M, ldy]
   void* y_op;                  // SiluMul: model dtype [M, ldy]
   int ldy;
   float* ss_out;               // Store / AddTo (MFMA kernel): [Nout / 16, M] row sums of y^2 per 16-column tile
+  // Store / AddTo on packed weights without ss_out: when set, the kernel may
+  // split K over `splits` workgroups and leave part[z][m][n] (stride ldy)
+  // instead of writing y; the caller then forms y = (AddTo ? y : 0) + sum_z part[z]
+  float* part;
   float* logits;               // Argmax: optional fp32 [M, Nout]
   Top2* partials;              // Argmax: [M, grid_x]
   RopeOut rope;                // QkvRope
   int grid_x;                  // filled by the launcher
+  int splits;                  // filled by the launcher: K splits left in part (1: y written)
 };
+constexpr int kMaxSplits = 8;
 // Kernel families: LDS-staged dot2 GEMV (M <= 8 per slice, fp32), weight-streaming
 // MFMA (bf16, 8 < M <= 16), tiled MFMA GEMM (bf16, M > 16, K % 64 == 0).
 enum class ProjKernel { Lds = 0, Skinny = 1, Tiled = 2 };
@@ -106,11 +116,31 @@ int gemv_grid_x(int M, int Nout, Epi epi, DType dt, int num_cus, int K);
 size_t gemv_lds_bytes(int M, int K, DType dt);  // dynamic LDS of the chosen kernel
 bool gemv_uses_mfma(int M, int K, DType dt);
 
+// Packed copy of W for the weight-streaming MFMA kernel: ceil(Nout / 16) tiles
+// of K / 32 fragments; fragment (t, s) is 1 KiB at byte (t * K/32 + s) * 1024,
+// its 16-byte piece l holding W[row(t, l % 16)][32 s + 8 (l / 16) .. + 8], row
+// t*16 + c, or for rope_d > 0 the q/k/v order that puts rotary pairs (j, j+d/2)
+// of one head in columns c and c + 8 of a tile.  Rows past Nout are zero.
+struct PackArgs {
+  void* dst;
+  const void *w_a, *w_b, *w_c;  // rows [0, n_a), [n_a, n_a + n_b), the rest
+  int n_a, n_b, Nout, K, rope_d;
+};
+size_t packed_bytes(int Nout, int K);
+hipError_t launch_pack(const PackArgs& p, hipStream_t s);
+
 // ---------------------------------------------------------------- small kernels
 hipError_t launch_build_fc_input(DType dt, int N, int H, const int32_t* ids, const void* embed,
                                  const void* draft_hidden, void* out, hipStream_t s);
-hipError_t launch_rmsnorm(DType dt, int rows, int H, const int32_t* row_idx, const float* x, const void* gain,
-                          float eps, void* out, hipStream_t s, const int32_t* live = nullptr);
+// out[i] = RMSNorm(x[r]) * gain, r = row_idx ? row_idx[i] : i; H <= kMaxHidden.
+// With nsplit > 0 the row is first completed from split partials and written
+// back: x[r] = (accumulate ? x[r] : 0) + sum_z part[z][r] (z in order; split z
+// starts at part + z * part_rows * H).
+constexpr int kMaxHidden = 8192;
+hipError_t launch_rmsnorm(DType dt, int rows, int H, const int32_t* row_idx, float* x, const void* gain,
+                          float eps, void* out, hipStream_t s, const int32_t* live = nullptr,
+                          const float* part = nullptr, int nsplit = 0, int part_rows = 0,
+                          bool accumulate = false);
 
 struct RopeArgs {
   int N, n_q, n_kv, d, block_size;

@@ -22,31 +22,63 @@ __global__ __launch_bounds__(256) void fc_input_kernel(int H_bytes, const int32_
 }
 
 // out[i] = x[row] / sqrt(mean(x[row]^2) + eps) * gain, rounded to the operand
-// dtype; one workgroup per row, row = row_idx ? row_idx[i] : i.
-template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(int H, const int32_t* __restrict__ row_idx,
-                                                      const float* __restrict__ x, const T* __restrict__ gain,
-                                                      float eps, T* __restrict__ out,
-                                                      const int32_t* __restrict__ live) {
-  __shared__ float part[4];
+// dtype; one workgroup per row, row = row_idx ? row_idx[i] : i.  With NS > 0
+// the row is first completed from the split partials of the projection that
+// produced it, x[row] = (accumulate ? x[row] : 0) + part[0][row] + part[1][row]
+// + ..., summed in split order and written back as the new residual row.
+// Every thread holds at most two 16-byte pieces of the row and issues all of
+// their loads (residual and partials) before the first add.
+template <typename T, int NS>
+__global__ __launch_bounds__(1024) void rmsnorm_kernel(int H, const int32_t* __restrict__ row_idx,
+                                                       float* __restrict__ x, const T* __restrict__ gain,
+                                                       float eps, T* __restrict__ out,
+                                                       const int32_t* __restrict__ live,
+                                                       const float* __restrict__ part, int64_t part_stride,
+                                                       int accumulate) {
+  __shared__ float wave_ss[16];
   const int i = blockIdx.x;
   if (live && i >= *live) return;  // padding row of the compacted layout
   const int r = row_idx ? row_idx[i] : i;
-  const f32x4* xr = reinterpret_cast<const f32x4*>(x + static_cast<int64_t>(r) * H);
+  f32x4* xr = reinterpret_cast<f32x4*>(x + static_cast<int64_t>(r) * H);
   const int nv = H / 4;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 keep[2];
   float ss = 0.f;
-  for (int v = threadIdx.x; v < nv; v += 256) {
-    const f32x4 q = xr[v];
-    ss += q[0] * q[0] + q[1] * q[1] + q[2] * q[2] + q[3] * q[3];
+  {
+    f32x4 xv[2], pv[2][NS > 0 ? NS : 1];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int v = min(static_cast<int>(threadIdx.x + blockDim.x * u), nv - 1);
+      xv[u] = NS == 0 || accumulate ? xr[v] : zero;
+#pragma unroll
+      for (int z = 0; z < NS; ++z)
+        pv[u][z] = reinterpret_cast<const f32x4*>(part + z * part_stride + static_cast<int64_t>(r) * H)[v];
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      f32x4 q = xv[u];
+#pragma unroll
+      for (int z = 0; z < NS; ++z) q += pv[u][z];
+      const bool mine = static_cast<int>(threadIdx.x + blockDim.x * u) < nv;
+      q = mine ? q : zero;
+      if (NS > 0 && mine) xr[threadIdx.x + blockDim.x * u] = q;
+      keep[u] = q;
+      ss += q[0] * q[0] + q[1] * q[1] + q[2] * q[2] + q[3] * q[3];
+    }
   }
   ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  const int nw = blockDim.x >> 6;
+  if ((threadIdx.x & 63) == 0) wave_ss[threadIdx.x >> 6] = ss;
   __syncthreads();
-  ss = part[0] + part[1] + part[2] + part[3];
+  ss = 0.f;
+  for (int w = 0; w < nw; ++w) ss += wave_ss[w];
   const float scale = 1.f / sqrtf(ss / static_cast<float>(H) + eps);
   T* o = out + static_cast<int64_t>(i) * H;
-  for (int v = threadIdx.x; v < nv; v += 256) {
-    const f32x4 q = xr[v];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int v = threadIdx.x + blockDim.x * u;
+    if (v >= nv) continue;
+    const f32x4 q = keep[u];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       o[4 * v + e] = Elem<T>::from_f32(q[e] * scale * Elem<T>::to_f32(gain[4 * v + e]));
@@ -142,16 +174,47 @@ hipError_t launch_build_fc_input(DType dt, int N, int H, const int32_t* ids, con
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm(DType dt, int rows, int H, const int32_t* row_idx, const float* x, const void* gain,
-                          float eps, void* out, hipStream_t s, const int32_t* live) {
-  dim3 grid(rows);
-  if (dt == DType::F32)
-    hipLaunchKernelGGL(rmsnorm_kernel<float>, grid, dim3(256), 0, s, H, row_idx, x,
-                       static_cast<const float*>(gain), eps, static_cast<float*>(out), live);
-  else
-    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, grid, dim3(256), 0, s, H, row_idx, x,
-                       static_cast<const bf16_t*>(gain), eps, static_cast<bf16_t*>(out), live);
+namespace {
+template <typename T, int NS>
+void launch_rmsnorm_t(int rows, int H, const int32_t* row_idx, float* x, const void* gain, float eps, void* out,
+                      hipStream_t s, const int32_t* live, const float* part, int64_t stride, bool accumulate) {
+  const int nv = H / 4;
+  int threads = ((nv + 1) / 2 + 63) / 64 * 64;  // at most two pieces per thread
+  if (threads < 64) threads = 64;
+  if (nv <= 1024) threads = (nv + 63) / 64 * 64;  // one piece per thread while that fits
+  hipLaunchKernelGGL((rmsnorm_kernel<T, NS>), dim3(rows), dim3(threads), 0, s, H, row_idx, x,
+                     static_cast<const T*>(gain), eps, static_cast<T*>(out), live, part, stride, int(accumulate));
+}
+
+template <typename T>
+hipError_t launch_rmsnorm_dt(int rows, int H, const int32_t* row_idx, float* x, const void* gain, float eps,
+                             void* out, hipStream_t s, const int32_t* live, const float* part, int nsplit,
+                             int64_t stride, bool accumulate) {
+  switch (nsplit) {
+    case 0: launch_rmsnorm_t<T, 0>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate); break;
+    case 1: launch_rmsnorm_t<T, 1>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate); break;
+    case 2: launch_rmsnorm_t<T, 2>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate); break;
+    case 3: launch_rmsnorm_t<T, 3>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate); break;
+    case 4: launch_rmsnorm_t<T, 4>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate); break;
+    case 5: launch_rmsnorm_t<T, 5>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate); break;
+    case 6: launch_rmsnorm_t<T, 6>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate); break;
+    case 7: launch_rmsnorm_t<T, 7>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate); break;
+    case 8: launch_rmsnorm_t<T, 8>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_rmsnorm(DType dt, int rows, int H, const int32_t* row_idx, float* x, const void* gain,
+                          float eps, void* out, hipStream_t s, const int32_t* live, const float* part, int nsplit,
+                          int part_rows, bool accumulate) {
+  if (H % 4 != 0 || H > kMaxHidden || rows <= 0) return hipErrorInvalidValue;
+  if (nsplit > 0 && !part) return hipErrorInvalidValue;
+  const int64_t stride = static_cast<int64_t>(part_rows) * H;
+  if (dt == DType::F32)
+    return launch_rmsnorm_dt<float>(rows, H, row_idx, x, gain, eps, out, s, live, part, nsplit, stride, accumulate);
+  return launch_rmsnorm_dt<bf16_t>(rows, H, row_idx, x, gain, eps, out, s, live, part, nsplit, stride, accumulate);
 }
 
 hipError_t launch_rope_kvwrite(const RopeArgs& a, hipStream_t s) {

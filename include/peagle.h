@@ -108,12 +108,34 @@ typedef struct {
   const pe_layer_weights *layers;
 } pe_weights;
 
-typedef struct pe_model pe_model; /* opaque, immutable after creation, usable from any stream */
+typedef struct pe_model pe_model; /* opaque; usable from any stream once created (and packed) */
 
 /* Validate the description and weight pointers and build a model handle
  * (host memory only).  Returns PE_EINVAL / PE_EUNSUPPORTED on bad input. */
 pe_status pe_model_create(const pe_model_desc *desc, const pe_weights *weights, pe_model **out);
 void pe_model_destroy(pe_model *model);
+
+/* Bytes of device memory for the packed copy of the projection weights (fc and
+ * every layer's q/k/v, o, gate, up, down); 0 when the model has nothing to pack
+ * (fp32 weights, no layers, or hidden / n_q*head_dim / inter not multiples of
+ * 32 or head_dim not a multiple of 16). */
+size_t pe_packed_weights_bytes(const pe_model *model);
+
+/* Optional, for speed with few draft rows (at most 16 rows per pass, e.g. one
+ * sequence at K <= 8).  Copies the projection weights into `packed` in the
+ * fragment order of the bf16 matrix-core tiles (each 16-output x 32-input
+ * fragment one contiguous KiB, the q/k/v rows grouped in rotary pairs) and
+ * attaches the buffer to the model; from then on those projections stream it
+ * instead of the row-major weights (same products, same results up to the
+ * summation order of split partial sums).  `packed`: device buffer of at least
+ * pe_packed_weights_bytes() bytes, 256-byte aligned, owned by the caller, not
+ * modified and kept alive while the model is used; it snapshots the weights as
+ * they are when the copy runs on `stream` (later changes to the row-major
+ * weights are not seen).  Forward calls on other streams must be ordered after
+ * that work; do not call it while a pass using the model is in flight.
+ * Returns PE_OK (nothing to do when 0 bytes are needed), PE_EINVAL (null or
+ * misaligned buffer), PE_EWORKSPACE (too small), PE_EHIP. */
+pe_status pe_model_pack_weights(pe_model *model, void *packed, size_t packed_bytes, hipStream_t stream);
 
 /* Bytes of workspace pe_draft_forward needs for a batch of `num_seqs`
  * sequences, depth K and `num_rows` draft rows (0 on invalid input). */

@@ -30,9 +30,9 @@ def host_weights(spec, wseed, prep_only=False):
 _dev_cache = {}
 
 
-def device_model(spec, wseed, prep_only=False):
+def device_model(spec, wseed, prep_only=False, pack=True):
     import drafting_draft_expand_amd as pe
-    key = (spec, wseed, prep_only)
+    key = (spec, wseed, prep_only, pack)
     if key not in _dev_cache:
         if len(_dev_cache) >= 2:
             _dev_cache.clear()
@@ -43,7 +43,7 @@ def device_model(spec, wseed, prep_only=False):
             m = pe.DraftModel(spec.hidden, spec.vocab, 0, 1, 1, 16, 8, spec.dtype, dw,
                               mask_token_id=spec.mask_token_id)
         else:
-            m = pe.DraftModel.from_spec(spec, dw)
+            m = pe.DraftModel.from_spec(spec, dw, pack=pack)
         _dev_cache[key] = (m, dw)
     return _dev_cache[key][0]
 

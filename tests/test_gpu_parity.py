@@ -76,12 +76,12 @@ def test_prepare_sweep_bit_exact(dtype):
 
 
 # ----------------------------------------------------------------------------- forward
-def _forward_case(wl, seqs=None, batch=None, model_spec=None, wseed=None):
+def _forward_case(wl, seqs=None, batch=None, model_spec=None, wseed=None, pack=True):
     spec = model_spec or wl.model
     wseed = wl.wseed if wseed is None else wseed
-    _say(f"forward {wl.name} seqs={seqs}")
+    _say(f"forward {wl.name} seqs={seqs} pack={pack}")
     w = host_weights(spec, wseed)
-    model = device_model(spec, wseed)
+    model = device_model(spec, wseed, pack=pack)
     b = synth.make_batch(wl) if batch is None else batch
     db = upload_batch(b, "cuda:0")
     prep, tokens, logits, gap = gpu_round(model, db, b.K)
@@ -148,6 +148,26 @@ def test_forward_bf16_few_rows_unfused():
     separate gather / norm / RoPE kernels."""
     spec = synth.ModelSpec(hidden=256, vocab=1000, n_layers=1, n_q=8, n_kv=2, head_dim=64, inter=512)
     wl = synth.Workload("few-rows-bf16", spec, c=1, K=3, ctx_lo=30, ctx_hi=90, accept_hi=3, seed=43)
+    _forward_case(wl)
+
+
+@pytest.mark.parametrize("pack", [True, False])
+@pytest.mark.parametrize("K", [5, 8])
+def test_forward_bf16_few_rows_mfma(K, pack):
+    """One sequence, 9..16 draft rows: the weight-streaming MFMA projections,
+    on the packed copy (tile groups of 1, 2 and 4 with ragged ends, fc split
+    over K into partials that the RMSNorm adds up) and on row-major weights."""
+    spec = synth.ModelSpec(hidden=544, vocab=1000, n_layers=1, n_q=6, n_kv=2, head_dim=32, inter=5120)
+    wl = synth.Workload(f"few-rows-mfma-k{K}", spec, c=1, K=K, ctx_lo=40, ctx_hi=200, accept_hi=K, seed=60 + K)
+    _forward_case(wl, pack=pack)
+
+
+def test_forward_two_layer_bf16_mfma_splits():
+    """Two layers at 14 rows, every projection split over K where allowed: the
+    second layer's first RMSNorm adds the first layer's down-projection
+    partials to the residual rows."""
+    spec = synth.ModelSpec(hidden=1024, vocab=700, n_layers=2, n_q=8, n_kv=2, head_dim=64, inter=2048)
+    wl = synth.Workload("two-layer-mfma", spec, c=1, K=7, ctx_lo=20, ctx_hi=300, accept_hi=7, seed=66)
     _forward_case(wl)
 
 
