@@ -55,7 +55,7 @@ int attention_splits(int c, int n_kv) {
   const int base = c * n_kv;
   int s = (1024 + base - 1) / base;
   if (s < 1) s = 1;
-  if (s > 16) s = 16;
+  if (s > pe::kAttnMaxSplits) s = pe::kAttnMaxSplits;
   return s;
 }
 
@@ -65,10 +65,9 @@ struct Workspace {
   int splits, lm_parts;
 };
 
-// Split partials of the few-row projections that write the residual rows.
-inline size_t part_bytes(const pe_model_desc& d, int N) {
-  return N <= 16 ? size_t(pe::kMaxSplits) * N * d.hidden * 4 : 0;
-}
+// Split partials of the projections that write the residual rows (the next
+// RMSNorm adds them up).
+inline size_t part_bytes(const pe_model_desc& d, int N) { return size_t(pe::kMaxSplits) * N * d.hidden * 4; }
 
 Workspace plan_workspace(const pe_model* m, int c, int K, int N) {
   const pe_model_desc& d = m->d;
@@ -399,7 +398,7 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
   pe::Top2* top2 = reinterpret_cast<pe::Top2*>(wb + ws.top2);
   void* f = wb + ws.f;
   float* ss0 = reinterpret_cast<float*>(wb + ws.ss0);
-  float* xpart = part_bytes(d, N) ? reinterpret_cast<float*>(wb + ws.part) : nullptr;
+  float* xpart = reinterpret_cast<float*>(wb + ws.part);
   const int cus = num_cus(m);
 
   const int ss_tiles = (H + 15) / 16;
@@ -431,7 +430,9 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
   int pend_splits = 0;
   bool pend_acc = false;
   auto into_x = [&](pe::GemvArgs& g, pe::Epi e) -> pe_status {
-    g.part = packed && g.pk_a && !g.ss_out ? xpart : nullptr;
+    // the weight-streaming kernel splits only packed weights; the tiled GEMM
+    // splits when its tiles alone would leave CUs idle
+    g.part = !g.ss_out && (g.pk_a || pe::proj_kernel(g.M, g.K, t) == pe::ProjKernel::Tiled) ? xpart : nullptr;
     pe_status r = proj(g, e);
     if (r != PE_OK) return r;
     pend_splits = g.splits > 1 ? g.splits : 0;

@@ -377,30 +377,48 @@ __global__ __launch_bounds__(512, OCC) void attn_mfma_kernel(AttnArgs a) {
 }
 
 // out[row, h, :] = sum_s acc_s * e^{m_s - M} / sum_s l_s * e^{m_s - M};
-// one 64-thread workgroup per (row, head), split weights shared through LDS.
-template <typename T>
+// one 64-thread workgroup per (row, head).  Every load is issued before the
+// first use: lane s reads the statistics of split s, and every lane reads its
+// output dims (lane, lane + 64) of all splits, splits past S clamped to the
+// last one and weighted 0, so the kernel waits for memory once.
+template <typename T, int D>
 __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
-  __shared__ float wgt[64];
+  constexpr int DV = (D + 63) / 64;  // output dims per lane
   const int row = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-  const int D = a.d, S = a.splits;
+  const int S = a.splits;
   T* out = static_cast<T*>(a.out) + (static_cast<int64_t>(row) * a.n_q + h) * D;
   if (a.rejected[row]) {
     for (int dd = lane; dd < D; dd += 64) out[dd] = Elem<T>::from_f32(0.f);
     return;
   }
   const float* p = a.partial + (static_cast<int64_t>(row) * a.n_q + h) * S * (D + 2);
-  const float ms = lane < S ? p[lane * (D + 2) + D] : -INFINITY;
+  const int sl = min(lane, S - 1);
+  const float m_l = p[sl * (D + 2) + D];
+  const float l_l = p[sl * (D + 2) + D + 1];
+  float v[DV][kAttnMaxSplits];
+#pragma unroll
+  for (int z = 0; z < kAttnMaxSplits; ++z) {
+    const int zc = min(z, S - 1);
+#pragma unroll
+    for (int e = 0; e < DV; ++e) v[e][z] = p[zc * (D + 2) + min(lane + 64 * e, D - 1)];
+  }
+  const float ms = lane < S ? m_l : -INFINITY;
   const float M = wave_max(ms);
   const float w = ms == -INFINITY ? 0.f : expf(ms - M);
-  const float den = wave_sum(lane < S ? w * p[lane * (D + 2) + D + 1] : 0.f);
-  wgt[lane] = w;
-  __syncthreads();
-  const float inv = 1.f / den;
-  for (int dd = lane; dd < D; dd += 64) {
-    float num = 0.f;
-    for (int s = 0; s < S; ++s) num = fmaf(p[s * (D + 2) + dd], wgt[s], num);
-    out[dd] = Elem<T>::from_f32(num * inv);
+  const float den = wave_sum(lane < S ? w * l_l : 0.f);
+  float num[DV];
+#pragma unroll
+  for (int e = 0; e < DV; ++e) num[e] = 0.f;
+#pragma unroll
+  for (int z = 0; z < kAttnMaxSplits; ++z) {
+    const float wz = __shfl(w, z, 64);  // 0 for splits past S
+#pragma unroll
+    for (int e = 0; e < DV; ++e) num[e] = fmaf(v[e][z], wz, num[e]);
   }
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int e = 0; e < DV; ++e)
+    if (lane + 64 * e < D) out[lane + 64 * e] = Elem<T>::from_f32(num[e] * inv);
 }
 
 template <int D>
@@ -416,6 +434,7 @@ void launch_mfma(const AttnArgs& a, dim3 grid, hipStream_t s) {
 
 template <typename T>
 hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
+  if (a.splits < 1 || a.splits > kAttnMaxSplits || a.d > 128) return hipErrorInvalidValue;
   dim3 grid(a.splits, a.n_kv, a.c);
   if (sizeof(T) == 2 && (a.d == 64 || a.d == 128)) {
     if (a.d == 64)
@@ -432,7 +451,13 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel<T>, dim3(a.N, a.n_q), dim3(64), 0, s, a);
+  const dim3 cgrid(a.N, a.n_q);
+  switch (a.d) {
+    case 16: hipLaunchKernelGGL((attn_combine_kernel<T, 16>), cgrid, dim3(64), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((attn_combine_kernel<T, 32>), cgrid, dim3(64), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((attn_combine_kernel<T, 64>), cgrid, dim3(64), 0, s, a); break;
+    default: hipLaunchKernelGGL((attn_combine_kernel<T, 128>), cgrid, dim3(64), 0, s, a); break;
+  }
   return hipGetLastError();
 }
 

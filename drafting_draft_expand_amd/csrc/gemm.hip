@@ -77,11 +77,13 @@ __device__ __forceinline__ int lds_off(int r, int c) {
 // 16 x 16 block.  red is LDS scratch for WGN * BM candidates (argmax only).
 template <int BM, int BN, int WGM, int WGN, int TM, int TN, Epi EPI>
 __device__ __forceinline__ void tile_epilogue(const GemvArgs& a, f32x4 (&acc)[TM][TN], int m0, int nt, int num_n,
-                                              int wm, int wn, Top2* red) {
+                                              int wm, int wn, Top2* red, int z, int splits) {
   constexpr int WM = TM * 16, WN = TN * 16, NT = WGM * WGN * 64;
   const int tid = threadIdx.x, lane = tid & 63;
   const int l16 = lane & 15, lq = lane >> 4;
   if constexpr (EPI == Epi::Store || EPI == Epi::AddTo) {
+    // K split over workgroups: the sum of this split goes to part[z]
+    float* out = splits > 1 ? a.part + static_cast<int64_t>(z) * a.M * a.ldy : a.y;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -91,8 +93,8 @@ __device__ __forceinline__ void tile_epilogue(const GemvArgs& a, f32x4 (&acc)[TM
         for (int q = 0; q < 4; ++q) {
           const int m = m0 + wm * WM + i * 16 + lq * 4 + q;
           if (m >= a.M || n >= a.Nout) continue;
-          float* y = a.y + static_cast<int64_t>(m) * a.ldy + n;
-          if constexpr (EPI == Epi::AddTo) *y += acc[i][jn][q];
+          float* y = out + static_cast<int64_t>(m) * a.ldy + n;
+          if (EPI == Epi::AddTo && splits == 1) *y += acc[i][jn][q];
           else *y = acc[i][jn][q];
         }
       }
@@ -194,7 +196,8 @@ __device__ __forceinline__ void tile_epilogue(const GemvArgs& a, f32x4 (&acc)[TM
 }
 
 template <int BM, int BN, int BK, int PD, int WGM, Epi EPI, AMode MODE>
-__global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel(GemvArgs a, int num_m, int num_n) {
+__global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel(GemvArgs a, int num_m, int num_n,
+                                                                                  int splits) {
   constexpr int WGN = 4 / WGM;                // wave grid WGM x WGN
   constexpr int WM = BM / WGM, WN = BN / WGN; // wave block
   constexpr int TM = WM / 16, TN = WN / 16;   // MFMA tiles per wave
@@ -208,15 +211,20 @@ __global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel
   __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * LDT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WGM, wn = wave / WGM;
-  // XCD-aware tile order: the M tiles of one W tile land on one XCD
-  const int total = num_m * num_n;
+  // XCD-aware tile order: the M tiles of one (W tile, K split) land on one XCD
+  const int total = num_m * num_n * splits;
   const int per_xcd = (total + 7) / 8;
   const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   if (L >= total) return;
-  const int mt = L % num_m, nt = L / num_m;
+  const int mt = L % num_m, rest = L / num_m;
+  const int z = rest % splits, nt = rest / splits;
   const int m0 = mt * BM;
   if (a.m_live && m0 >= *a.m_live) return;  // only padding rows in this tile
-  const int nk = a.K / BK;
+  // this workgroup's K steps: [kbase, kbase + nk) of the K / BK steps
+  const int nk_all = a.K / BK;
+  const int per_split = (nk_all + splits - 1) / splits;
+  const int kbase = min(nk_all, z * per_split);
+  const int nk = min(nk_all, kbase + per_split) - kbase;
 
   // thread -> 16-byte chunk mapping of the A and W tiles (rows of CPR chunks);
   // recomputed where used rather than held in registers
@@ -248,7 +256,7 @@ __global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel
   }
   auto fetch = [&](int kt, auto set_c) {
     constexpr int set = decltype(set_c)::value;
-    const int k0 = kt * BK;
+    const int k0 = (kbase + kt) * BK;
 #pragma unroll
     for (int i = 0; i < NA; ++i)
       if ((BM * CPR) % 256 == 0 || c_row + i * ROWS_PER_PASS < BM) {
@@ -322,7 +330,7 @@ __global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel
     __syncthreads();
   };
 
-  fetch(0, C0{});
+  fetch(0, C0{});  // every split has at least one K step (splits <= K / BK)
   if (PD == 2 && nk > 1) fetch(1, CS1{});
   stash(C0{}, C0{});
   if (PD == 1 && nk > 1) fetch(1, C0{});
@@ -335,7 +343,8 @@ __global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel
 
   // ---------------------------------------------------------------- epilogue
   static_assert(WGN * BM * sizeof(Top2) <= sizeof(Bs) / 2, "argmax scratch must fit one LDS buffer");
-  tile_epilogue<BM, BN, WGM, WGN, TM, TN, EPI>(a, acc, m0, nt, num_n, wm, wn, reinterpret_cast<Top2*>(&Bs[0][0]));
+  tile_epilogue<BM, BN, WGM, WGN, TM, TN, EPI>(a, acc, m0, nt, num_n, wm, wn, reinterpret_cast<Top2*>(&Bs[0][0]), z,
+                                               splits);
 }
 
 // Tile shapes (K step 32 for the 256-column tile, 64 for the others).
@@ -359,24 +368,43 @@ TileCfg pick_tile(int M, int Nout, Epi epi, int num_cus) {
   return kSmall;
 }
 
+// K splits for Store / AddTo when the tiles alone leave CUs idle and the
+// caller takes partial sums: enough for about two workgroups per CU, at most
+// kMaxSplits and at least 8 K steps per split.
+int gemm_splits(const GemvArgs& a, Epi epi, int tiles, int nk_all, int num_cus) {
+  if (!a.part || a.ss_out || (epi != Epi::Store && epi != Epi::AddTo)) return 1;
+  if (tiles >= 2 * num_cus) return 1;
+  int sp = (2 * num_cus + tiles - 1) / tiles;
+  if (sp > kMaxSplits) sp = kMaxSplits;
+  if (sp > nk_all / 8) sp = nk_all / 8;
+  return sp < 2 ? 1 : sp;
+}
+
 template <int BM, int BN, int BK, int PD, int WGM, Epi EPI, AMode MODE>
-hipError_t launch_t(GemvArgs& a, hipStream_t s) {
+hipError_t launch_t(GemvArgs& a, int num_cus, hipStream_t s) {
   const int num_m = (a.M + BM - 1) / BM;
   const int cols = EPI == Epi::SiluMul ? BN / 2 : BN;
   const int num_n = (a.Nout + cols - 1) / cols;
-  const int total = num_m * num_n;
+  const int splits = gemm_splits(a, EPI, num_m * num_n, a.K / BK, num_cus);
+  const int total = num_m * num_n * splits;
   const int grid = ((total + 7) / 8) * 8;
   a.grid_x = num_n;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, PD, WGM, EPI, MODE>), dim3(grid), dim3(256), 0, s, a, num_m, num_n);
+  a.splits = splits;
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, PD, WGM, EPI, MODE>), dim3(grid), dim3(256), 0, s, a, num_m, num_n,
+                     splits);
   return hipGetLastError();
 }
 
 template <Epi EPI, AMode MODE>
 hipError_t launch_cfg(GemvArgs& a, int num_cus, hipStream_t s) {
-  const TileCfg t = pick_tile(a.M, a.Nout, EPI, num_cus);
-  if (t.bn == 256) return launch_t<128, 256, 32, 2, 2, EPI, MODE>(a, s);
-  if (t.bn == 128) return launch_t<128, 128, 64, 1, 2, EPI, MODE>(a, s);
-  return launch_t<128, 64, 64, 1, 2, EPI, MODE>(a, s);
+  TileCfg t = pick_tile(a.M, a.Nout, EPI, num_cus);
+  // Store / AddTo into split partials: 128 x 128 tiles, K split to fill the CUs
+  if ((EPI == Epi::Store || EPI == Epi::AddTo) && a.part && !a.ss_out &&
+      tiles_of(t, a.M, a.Nout, EPI) < 2 * num_cus)
+    t = kMedium;
+  if (t.bn == 256) return launch_t<128, 256, 32, 2, 2, EPI, MODE>(a, num_cus, s);
+  if (t.bn == 128) return launch_t<128, 128, 64, 1, 2, EPI, MODE>(a, num_cus, s);
+  return launch_t<128, 64, 64, 1, 2, EPI, MODE>(a, num_cus, s);
 }
 
 }  // namespace

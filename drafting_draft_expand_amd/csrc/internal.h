@@ -158,6 +158,8 @@ hipError_t launch_rope_kvwrite(const RopeArgs& a, hipStream_t s);
 // Pages of one KV split that the bf16 MFMA attention keeps in LDS; with more
 // (max_blocks > (kAttnMaxPages - 8) * splits) it reads the block table instead.
 constexpr int kAttnMaxPages = 1088;
+// KV-range splits per (sequence, kv head): at most this many
+constexpr int kAttnMaxSplits = 16;
 
 struct AttnArgs {
   int c, N, n_q, n_kv, d, block_size, max_blocks, splits;

@@ -128,13 +128,23 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(RopeArgs a) {
 }
 
 // Merge the per-workgroup LM-head candidates of each sampled row: token =
-// best id (lowest id on ties), gap = best minus runner-up logit.
-__global__ __launch_bounds__(64) void argmax_finalize_kernel(int parts, const Top2* partials, int32_t* tokens,
-                                                             float* gap) {
+// best id (lowest id on ties), gap = best minus runner-up logit.  The merge is
+// order-independent; 256 threads read up to 1024 candidates per round, all
+// loads of a round issued before the first merge.
+__global__ __launch_bounds__(256) void argmax_finalize_kernel(int parts, const Top2* partials, int32_t* tokens,
+                                                              float* gap) {
+  __shared__ Top2 red[4];
   const int s = blockIdx.x;
-  const int lane = threadIdx.x;
+  const Top2* row = partials + static_cast<int64_t>(s) * parts;
   Top2 best = top2_empty();
-  for (int p = lane; p < parts; p += 64) best = top2_merge(best, partials[static_cast<int64_t>(s) * parts + p]);
+  for (int p0 = 0; p0 < parts; p0 += 1024) {
+    Top2 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = row[min(p0 + static_cast<int>(threadIdx.x) + 256 * u, parts - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (p0 + static_cast<int>(threadIdx.x) + 256 * u < parts) best = top2_merge(best, v[u]);
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     Top2 o;
@@ -144,7 +154,10 @@ __global__ __launch_bounds__(64) void argmax_finalize_kernel(int parts, const To
     o.pad = 0;
     best = top2_merge(best, o);
   }
-  if (lane == 0) {
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    best = top2_merge(top2_merge(red[0], red[1]), top2_merge(red[2], red[3]));
     tokens[s] = best.i1;
     if (gap) gap[s] = best.v1 - best.v2;
   }
@@ -152,16 +165,26 @@ __global__ __launch_bounds__(64) void argmax_finalize_kernel(int parts, const To
 
 // Greedy acceptance: longest prefix where draft == target, then the bonus
 // token ("P-EAGLE: Parallel Speculative Decoding in vLLM", Acceptance Length).
+// The K comparisons have no early exit, so all loads go out together.
 __global__ __launch_bounds__(256) void accept_kernel(int c, int K, const int32_t* draft, const int32_t* target,
                                                      int32_t* acc, int32_t* bonus) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= c) return;
   const int32_t* d = draft + static_cast<int64_t>(i) * K;
   const int32_t* t = target + static_cast<int64_t>(i) * (K + 1);
-  int n = 0;
-  while (n < K && d[n] == t[n]) ++n;
+  int n = K;
+  int32_t b = t[K];
+#pragma unroll 8
+  for (int k = 0; k < K; ++k) {
+    const int32_t tk = t[k];
+    const bool miss = d[k] != tk;
+    if (n == K && miss) {
+      n = k;
+      b = tk;
+    }
+  }
   acc[i] = n;
-  bonus[i] = t[n];
+  bonus[i] = b;
 }
 
 }  // namespace
@@ -229,7 +252,8 @@ hipError_t launch_rope_kvwrite(const RopeArgs& a, hipStream_t s) {
 
 hipError_t launch_argmax_finalize(int S, int parts, const Top2* partials, int32_t* tokens, float* gap,
                                   hipStream_t s) {
-  hipLaunchKernelGGL(argmax_finalize_kernel, dim3(S), dim3(64), 0, s, parts, partials, tokens, gap);
+  if (parts < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(argmax_finalize_kernel, dim3(S), dim3(256), 0, s, parts, partials, tokens, gap);
   return hipGetLastError();
 }
 
