@@ -28,6 +28,7 @@ METRIC = "draft tokens/s per parallel-draft step (K=7, c=1/64); % of HBM/MFMA ro
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lm_head_traffic.json")
+DEFAULT_WORKLOAD = "gptoss20b-bf16-c1-k7"
 COPY_BYTES = 1 << 30
 
 
@@ -108,18 +109,114 @@ def _calibrate_copy() -> int:
     return 0
 
 
+PREP_WORKLOAD = "prep-bf16-c64-k7-h2880"
+PREP_SETS = 64
+
+
+def prep_bytes(spec, b, K) -> int:
+    """Algorithmic bytes of one expansion + placement: target hidden rows read
+    once, draft hidden rows written once, the metadata read and written once
+    (one block-table entry per draft row)."""
+    eb = 4 if spec.dtype == "fp32" else 2
+    c, T, N = b.c, b.T, b.N
+    meta = 4 * 3 * c + 8 * T + 4 * N + N * (4 + 4 + 8 + 1 + 1) + 4 * T + 4 * (c + 1) + 4 * c + 4 * c * K
+    return (T + N) * spec.hidden * eb + meta
+
+
+def _bench_prep(args) -> int:
+    """Time pe_prepare_draft_batch alone.  Every step uses the next of
+    PREP_SETS buffer sets (target hidden rows in, draft rows out), so the
+    working set (PREP_SETS x ~8 MB) exceeds the 256 MB memory-side cache and
+    every step reads and writes HBM."""
+    import torch
+    import drafting_draft_expand_amd as pe
+    import synth
+    from synth.device import upload_batch, upload_weights
+
+    wl = synth.WORKLOADS[PREP_WORKLOAD if args.workload == DEFAULT_WORKLOAD else args.workload]
+    spec, K = wl.model, wl.K
+    dev = "cuda:0"
+    w = synth.make_weights(spec, wl.wseed, prep_only=True)
+    dw = upload_weights(w, dev)
+    model = pe.DraftModel(spec.hidden, spec.vocab, 0, 1, 1, 16, 8, spec.dtype, dw, mask_token_id=spec.mask_token_id)
+    b = synth.make_batch(wl)
+    db = upload_batch(b, dev)
+    stream = torch.cuda.current_stream()
+    hid = [db["target_hidden"].clone() for _ in range(PREP_SETS)]
+    outs = []
+    for s in range(PREP_SETS):
+        outs.append(pe.prepare_draft_batch(model, K, db["query_lens"], db["target_ids"], db["target_pos"],
+                                           db["num_accepted"], db["bonus_ids"], hid[s], db["block_table"],
+                                           stream=stream))
+    torch.cuda.synchronize()
+    it = [0]
+
+    def step():
+        s = it[0] % PREP_SETS
+        it[0] += 1
+        pe.prepare_draft_batch(model, K, db["query_lens"], db["target_ids"], db["target_pos"], db["num_accepted"],
+                               db["bonus_ids"], hid[s], db["block_table"], out=outs[s], stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    model.timing_enable(pe.PE_KERNEL_PREPARE, True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    k_ms, k_n = model.timing_read(pe.PE_KERNEL_PREPARE)
+    model.timing_enable(pe.PE_KERNEL_PREPARE, False)
+    k_s = k_ms / max(k_n, 1) / 1e3
+    nbytes = prep_bytes(spec, b, K)
+    gbs = nbytes / (ms / 1e3) / 1e9
+    print(f"# prep {wl.name}: {ms * 1e3:.2f} us/step launch-inclusive, {k_s * 1e6:.2f} us per launch (events)",
+          file=sys.stderr, flush=True)
+    out = {
+        "metric": "draft-batch expansion + hidden placement throughput (a1-a3)",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "launch_mode": "eager",
+        "mode": "prep",
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if spec.dtype == "bf16" else "f32",
+        "data": f"synthetic: N(0,1) target hidden states and h_shared, uniform accepted counts, "
+                f"{PREP_SETS} rotated buffer sets",
+        "config": {"workload": wl.name, "num_seqs": b.c, "draft_depth": K, "target_rows": b.T, "draft_rows": b.N,
+                   "hidden": spec.hidden},
+        "roofline": {"bound": "hbm", "kernel": "prepare", "achieved": round(nbytes / k_s / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(nbytes / k_s / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": nbytes, "avg_launch_us": round(k_s * 1e6, 2),
+                     "launches": k_n},
+    }
+    model.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="gptoss20b-bf16-c1-k7")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--eager", action="store_true", help="time eager launches only (no HIP graph replay)")
-    ap.add_argument("--mode", choices=("peagle", "ar", "loop"), default="peagle",
+    ap.add_argument("--mode", choices=("peagle", "ar", "loop", "prep"), default="peagle",
                     help="peagle: one parallel-draft round per step; ar: the K-pass autoregressive baseline "
-                         "on the same kernels; loop: rounds chained through the device-built next batch")
+                         "on the same kernels; loop: rounds chained through the device-built next batch; "
+                         "prep: the batch expansion and hidden placement alone (default workload "
+                         f"{PREP_WORKLOAD}), over {PREP_SETS} rotated buffer sets")
     ap.add_argument("--layout", choices=("fixed", "compact"), default="fixed",
                     help="draft layout: fixed (rejected rows kept as inert rows) or compact (dropped)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -131,6 +228,8 @@ def main() -> int:
         return 2
     if args.calibrate_copy:
         return _calibrate_copy()
+    if args.mode == "prep":
+        return _bench_prep(args)
 
     import torch
     import drafting_draft_expand_amd as pe

@@ -8,12 +8,14 @@ Public API (thin ctypes binding over libpeagle.so; all work runs in HIP):
 * :func:`accept` -- greedy accepted length and next bonus token
 * :func:`draft_autoregressive` -- the K-pass autoregressive baseline on the same kernels
 * :func:`next_verified_batch` -- next round's verified batch from this round's results
+* :func:`check_verified_batch` -- device check of a verified batch's preconditions
 """
 
 from ._lib import (  # noqa: F401
     DraftModel,
     PeError,
     accept,
+    check_verified_batch,
     draft_autoregressive,
     draft_forward,
     load,
@@ -23,4 +25,9 @@ from ._lib import (  # noqa: F401
     PE_KERNEL_LM_HEAD,
     PE_KERNEL_PREPARE,
     PE_KERNEL_ATTENTION,
+    PE_CHECK_QUERY_LEN,
+    PE_CHECK_ACCEPTED,
+    PE_CHECK_TOKEN_ID,
+    PE_CHECK_POSITION,
+    PE_CHECK_BLOCK_TABLE,
 )

@@ -24,7 +24,8 @@ PE_KERNEL_LM_HEAD, PE_KERNEL_PREPARE, PE_KERNEL_ATTENTION = 0, 1, 2
 EXPORTED = ("pe_model_create", "pe_model_destroy", "pe_workspace_bytes", "pe_prepare_draft_batch",
             "pe_draft_forward", "pe_accept", "pe_status_string", "pe_timing_enable", "pe_timing_read",
             "pe_autoregressive_workspace_bytes", "pe_draft_autoregressive", "pe_next_verified_batch",
-            "pe_prepare_draft_batch_compact", "pe_packed_weights_bytes", "pe_model_pack_weights")
+            "pe_prepare_draft_batch_compact", "pe_packed_weights_bytes", "pe_model_pack_weights",
+            "pe_check_verified_batch")
 
 
 class PeError(RuntimeError):
@@ -65,6 +66,8 @@ def load() -> ctypes.CDLL:
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.pe_model_create.argtypes = [ctypes.POINTER(ModelDesc), ctypes.POINTER(Weights), ctypes.POINTER(P)]
     lib.pe_model_create.restype = I32
+    lib.pe_check_verified_batch.argtypes = [P, I32, I32, I32] + [P] * 6 + [I32, P, P]
+    lib.pe_check_verified_batch.restype = I32
     lib.pe_packed_weights_bytes.argtypes = [P]
     lib.pe_packed_weights_bytes.restype = SZ
     lib.pe_model_pack_weights.argtypes = [P, P, SZ, P]
@@ -281,6 +284,27 @@ def draft_autoregressive(model: DraftModel, K: int, query_lens: torch.Tensor, ta
         workspace.numel() * workspace.element_size(), _ptr(tokens), _stream(stream))
     _check(st, "pe_draft_autoregressive")
     return tokens
+
+
+PE_CHECK_QUERY_LEN, PE_CHECK_ACCEPTED, PE_CHECK_TOKEN_ID, PE_CHECK_POSITION, PE_CHECK_BLOCK_TABLE = 1, 2, 4, 8, 16
+
+
+def check_verified_batch(model: DraftModel, K: int, query_lens: torch.Tensor, target_ids: torch.Tensor,
+                         target_pos: torch.Tensor, num_accepted: torch.Tensor, bonus_ids: torch.Tensor,
+                         block_table: torch.Tensor, error_bits: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """Device check of the verified batch (see pe_check_verified_batch).
+    Returns the int32 [1] device word of PE_CHECK_* bits (zeroed here when not
+    given, accumulated into when given)."""
+    c = int(query_lens.numel())
+    if error_bits is None:
+        error_bits = torch.zeros(1, dtype=torch.int32, device=query_lens.device)
+    st = load().pe_check_verified_batch(
+        model.handle, c, K, int(target_ids.numel()), _ptr(query_lens), _ptr(target_ids), _ptr(target_pos),
+        _ptr(num_accepted), _ptr(bonus_ids), _ptr(block_table), int(block_table.shape[1]), _ptr(error_bits),
+        _stream(stream))
+    _check(st, "pe_check_verified_batch")
+    return error_bits
 
 
 def next_verified_batch(K: int, kv_lens: torch.Tensor, bonus_ids: torch.Tensor, draft_tokens: torch.Tensor,

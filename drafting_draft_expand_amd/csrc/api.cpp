@@ -49,11 +49,12 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline DType dt(const pe_model* m) { return m->d.dtype == PE_F32 ? DType::F32 : DType::BF16; }
 
-// KV-range splits per (sequence, kv head): enough workgroups to cover the
-// chip at low concurrency without multiplying the partial-result traffic.
+// KV-range splits per (sequence, kv head): about 2048 workgroups (eight per
+// CU over the launch) so that the per-tile softmax work of long contexts
+// spreads over the chip, without multiplying the partial-result traffic.
 int attention_splits(int c, int n_kv) {
   const int base = c * n_kv;
-  int s = (1024 + base - 1) / base;
+  int s = (2048 + base - 1) / base;
   if (s < 1) s = 1;
   if (s > pe::kAttnMaxSplits) s = pe::kAttnMaxSplits;
   return s;
@@ -356,6 +357,26 @@ pe_status pe_prepare_draft_batch_compact(const pe_model* m, int32_t c, int32_t K
   return prepare_impl(m, c, K, T, query_lens, target_ids, target_pos, num_accepted, bonus_ids, target_hidden,
                       block_table, max_blocks, draft_ids, draft_pos, slot_mapping, is_rejected, is_masked,
                       hidden_map, cu_draft, kv_lens, sample_idx, draft_hidden, stream, 1);
+}
+
+pe_status pe_check_verified_batch(const pe_model* m, int32_t c, int32_t K, int32_t T, const int32_t* query_lens,
+                                  const int32_t* target_ids, const int32_t* target_pos, const int32_t* num_accepted,
+                                  const int32_t* bonus_ids, const int32_t* block_table, int32_t max_blocks,
+                                  int32_t* error_bits, hipStream_t stream) {
+  if (!m || c <= 0 || K <= 0 || T < c || max_blocks <= 0) return PE_EINVAL;
+  const void* ptrs[] = {query_lens, target_ids, target_pos, num_accepted, bonus_ids, block_table, error_bits};
+  for (const void* p : ptrs)
+    if (!p) return PE_EINVAL;
+  static_assert(PE_CHECK_QUERY_LEN == pe::kCheckQueryLen && PE_CHECK_ACCEPTED == pe::kCheckAccepted &&
+                    PE_CHECK_TOKEN_ID == pe::kCheckTokenId && PE_CHECK_POSITION == pe::kCheckPosition &&
+                    PE_CHECK_BLOCK_TABLE == pe::kCheckBlockTable,
+                "check bits");
+  pe::CheckArgs a{};
+  a.c = c; a.K = K; a.T = T; a.V = m->d.vocab > 0 ? m->d.vocab : INT32_MAX; a.max_blocks = max_blocks;
+  a.query_lens = query_lens; a.target_ids = target_ids; a.target_pos = target_pos;
+  a.num_accepted = num_accepted; a.bonus_ids = bonus_ids; a.block_table = block_table; a.error_bits = error_bits;
+  PE_HIP(pe::launch_check_batch(a, stream));
+  return PE_OK;
 }
 
 pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, const int32_t* draft_ids,

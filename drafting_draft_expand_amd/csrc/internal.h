@@ -40,6 +40,16 @@ struct PrepareArgs {
 };
 hipError_t launch_prepare(const PrepareArgs& a, hipStream_t s);
 
+// Device-side check of the expansion's preconditions (bits as in peagle.h).
+constexpr int kCheckQueryLen = 1, kCheckAccepted = 2, kCheckTokenId = 4, kCheckPosition = 8,
+              kCheckBlockTable = 16;
+struct CheckArgs {
+  int c, K, T, V, max_blocks;
+  const int32_t *query_lens, *target_ids, *target_pos, *num_accepted, *bonus_ids, *block_table;
+  int32_t* error_bits;
+};
+hipError_t launch_check_batch(const CheckArgs& a, hipStream_t s);
+
 // ---------------------------------------------------------------- projections
 enum class Epi { Store = 0, AddTo = 1, SiluMul = 2, Argmax = 3, QkvRope = 4 };
 

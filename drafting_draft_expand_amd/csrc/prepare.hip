@@ -113,18 +113,31 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepareArgs a, int row_byt
   const char* th = static_cast<const char*>(a.target_hidden);
   const char* hs = static_cast<const char*>(a.h_shared);
   char* out = static_cast<char*>(a.draft_hidden);
+  // four 16-byte pieces per thread and round, all loads issued before the
+  // stores (pieces past the end re-read the last one and are not stored)
   const int total = rows * width;
-  for (int f = threadIdx.x; f < total; f += blockDim.x) {
-    const int r = f / width;
-    const int v = v0 + f - r * width;
-    const char* src;
-    if (r > acc && r < acc + K) {
-      src = hs + v * 16;
-    } else {
-      const int j = r <= acc ? r : r - (K - 1);
-      src = th + static_cast<int64_t>(s + j) * row_bytes + v * 16;
+  constexpr int UP = 4;
+  for (int f0 = threadIdx.x; f0 < total; f0 += blockDim.x * UP) {
+    u32x4 val[UP];
+    int64_t dst[UP];
+#pragma unroll
+    for (int u = 0; u < UP; ++u) {
+      const int f = min(f0 + u * static_cast<int>(blockDim.x), total - 1);
+      const int r = f / width;
+      const int v = v0 + f - r * width;
+      const char* src;
+      if (r > acc && r < acc + K) {
+        src = hs + v * 16;
+      } else {
+        const int j = r <= acc ? r : r - (K - 1);
+        src = th + static_cast<int64_t>(s + j) * row_bytes + v * 16;
+      }
+      val[u] = load16(src);
+      dst[u] = static_cast<int64_t>(D + r) * row_bytes + v * 16;
     }
-    store16(out + static_cast<int64_t>(D + r) * row_bytes + v * 16, load16(src));
+#pragma unroll
+    for (int u = 0; u < UP; ++u)
+      if (f0 + u * static_cast<int>(blockDim.x) < total) store16(out + dst[u], val[u]);
   }
   const u32x4 zero = {0u, 0u, 0u, 0u};
   for (int f = threadIdx.x; f < npad * width; f += blockDim.x) {
@@ -133,7 +146,68 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepareArgs a, int row_byt
   }
 }
 
+// Device-side preconditions of the expansion, one block per sequence.  Every
+// value is range-checked before it is used as an index, so malformed input
+// only sets bits.
+__global__ __launch_bounds__(256) void check_batch_kernel(CheckArgs a) {
+  __shared__ int flags;
+  __shared__ int part[4];
+  const int i = blockIdx.x;
+  if (threadIdx.x == 0) flags = 0;
+  __syncthreads();
+  // first verified row of sequence i (lengths clamped into [0, T] for the sum)
+  int s = 0;
+  for (int j = threadIdx.x; j < i; j += blockDim.x) s += min(max(a.query_lens[j], 0), a.T);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+  __syncthreads();
+  s = part[0] + part[1] + part[2] + part[3];
+  int bits = 0;
+  if (i == 0 && threadIdx.x == 0) {
+    int64_t total = 0;
+    for (int j = 0; j < a.c; ++j) total += a.query_lens[j];
+    if (total != a.T) bits |= kCheckQueryLen;
+  }
+  const int L = a.query_lens[i];
+  const int acc = a.num_accepted[i];
+  const int bonus = a.bonus_ids[i];
+  bool ok = L >= 1 && s + L <= a.T;
+  if (!ok) bits |= kCheckQueryLen;
+  if (ok && (acc < 0 || acc > L - 1)) {
+    bits |= kCheckAccepted;
+    ok = false;
+  }
+  if (threadIdx.x == 0 && (bonus < 0 || bonus >= a.V)) bits |= kCheckTokenId;
+  if (ok) {
+    const int p0 = a.target_pos[s];
+    for (int j = threadIdx.x; j < L; j += blockDim.x) {
+      const int id = a.target_ids[s + j];
+      if (id < 0 || id >= a.V) bits |= kCheckTokenId;
+      const int p = a.target_pos[s + j];
+      if (p < 0 || p != p0 + j) bits |= kCheckPosition;
+    }
+    // every page the pass reads or writes: positions 0 .. target_pos[first + a_i] + K - 1
+    const int64_t last = static_cast<int64_t>(a.target_pos[s + acc]) + a.K - 1;
+    if (last < 0 || last / 16 >= a.max_blocks) {
+      bits |= kCheckBlockTable;
+    } else {
+      const int32_t* bt = a.block_table + static_cast<int64_t>(i) * a.max_blocks;
+      for (int q = threadIdx.x; q <= static_cast<int>(last / 16); q += blockDim.x)
+        if (bt[q] < 0) bits |= kCheckBlockTable;
+    }
+  }
+  if (bits) atomicOr(&flags, bits);
+  __syncthreads();
+  if (threadIdx.x == 0 && flags) atomicOr(a.error_bits, flags);
+}
+
 }  // namespace
+
+hipError_t launch_check_batch(const CheckArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(check_batch_kernel, dim3(a.c), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_prepare(const PrepareArgs& a, hipStream_t stream) {
   const int row_bytes = a.H * elem_bytes(a.dtype);

@@ -290,6 +290,37 @@ pe_status pe_next_verified_batch(int32_t num_seqs, int32_t K, const int32_t *kv_
                                  int32_t *target_pos_out, int32_t *num_accepted_out,
                                  int32_t *bonus_ids_out, hipStream_t stream);
 
+/* Check, on the device, the preconditions of pe_prepare_draft_batch that live
+ * in device memory (the host checks the rest): a debug aid for callers, which
+ * pe_prepare_draft_batch itself does not run.  [PP] Fused Triton Kernel lists
+ * the fields of the verified batch; the expansion assumes them well formed.
+ * Each violated condition ORs its bit into *error_bits (a device int32 the
+ * caller zeroes beforehand; the call never clears it, so checks accumulate):
+ *   PE_CHECK_QUERY_LEN    some L_i < 1, or the L_i do not sum to T
+ *   PE_CHECK_ACCEPTED     some a_i outside 0..L_i-1
+ *   PE_CHECK_TOKEN_ID     a target id or bonus id outside 0..V-1
+ *   PE_CHECK_POSITION     a negative position, or positions not consecutive
+ *                         within a sequence
+ *   PE_CHECK_BLOCK_TABLE  a page the pass reads or writes (positions up to
+ *                         target_pos[first + a_i] + K - 1) past max_blocks or
+ *                         mapped to a negative physical page
+ * The check reads only in-bounds locations of the given arrays: every value is
+ * range-checked before it is used as an index.  Whether a physical page lies
+ * inside the caller's cache cannot be checked (its size is not passed). */
+enum {
+  PE_CHECK_QUERY_LEN = 1,
+  PE_CHECK_ACCEPTED = 2,
+  PE_CHECK_TOKEN_ID = 4,
+  PE_CHECK_POSITION = 8,
+  PE_CHECK_BLOCK_TABLE = 16
+};
+pe_status pe_check_verified_batch(const pe_model *model, int32_t num_seqs, int32_t K,
+                                  int32_t total_target_rows, const int32_t *query_lens,
+                                  const int32_t *target_ids, const int32_t *target_pos,
+                                  const int32_t *num_accepted, const int32_t *bonus_ids,
+                                  const int32_t *block_table, int32_t max_blocks,
+                                  int32_t *error_bits, hipStream_t stream);
+
 /* Static description of a status code. */
 const char *pe_status_string(pe_status status);
 

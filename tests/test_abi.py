@@ -103,6 +103,14 @@ def test_calls_reject_bad_arguments_before_launch(lib):
         assert lib.pe_accept(0, 3, P, P, P, P, None) == -1
         assert lib.pe_accept(2, 3, None, P, P, P, None) == -1
         assert lib.pe_workspace_bytes(h, 0, 3, 12) == 0
+        # the device check refuses null pointers and empty batches before any launch
+        cargs = [h, 2, 3, 8] + [P] * 6 + [4, P, None]
+        bad = list(cargs)
+        bad[1] = 0
+        assert lib.pe_check_verified_batch(*bad) == -1
+        bad = list(cargs)
+        bad[11] = None
+        assert lib.pe_check_verified_batch(*bad) == -1
     finally:
         lib.pe_model_destroy(h)
 
