@@ -244,6 +244,9 @@ __global__ __launch_bounds__(512, OCC) void attn_mfma_kernel(AttnArgs a) {
     int wave_qmin = active ? qpos : 0x7fffffff;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) wave_qmin = min(wave_qmin, __shfl_xor(wave_qmin, off, 64));
+    // a wave whose 16 queries are all past the end or on rejected rows skips
+    // the products (it still stages its share of every K/V tile)
+    const bool wave_live = __builtin_amdgcn_readfirstlane(wave_qmin) != 0x7fffffff;
     u32x4 qf[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
@@ -350,7 +353,7 @@ __global__ __launch_bounds__(512, OCC) void attn_mfma_kernel(AttnArgs a) {
         constexpr int jj = decltype(j_c)::value;
         const int t = t0 + jj;
         if (t < ntiles) {
-          compute(t, std::integral_constant<int, jj & 1>{});
+          if (wave_live) compute(t, std::integral_constant<int, jj & 1>{});
           using Nb = std::integral_constant<int, (jj + 1) & 1>;
           using Ns = std::integral_constant<int, (jj + 1) % DEPTH>;
           // past the last tile these publish / request clamped, unused data

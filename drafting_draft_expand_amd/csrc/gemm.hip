@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel
   static_assert(CPR == 4 || CPR == 8, "K step 32 or 64");
   constexpr int NA = (BM * CPR + 255) / 256, NB = (BN * CPR + 255) / 256;  // chunks per thread
   static_assert(NA >= 1 && NB >= 1, "tile too small");
-  static_assert(PD == 1 || PD == 2, "prefetch distance 1 or 2");
+  static_assert(PD == 1 || PD == 2 || PD == 4, "prefetch distance 1, 2 or 4");
   __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * LDT];
   __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * LDT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -234,9 +234,10 @@ __global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel
   // W rows of one pass are consecutive except where a segment or the gate/up
   // pairing switches; those cases take the general pointer per chunk.
   constexpr bool W_CONTIG = EPI == Epi::Store || EPI == Epi::AddTo || EPI == Epi::Argmax;
-  // Global loads run PD K steps ahead of the MFMAs.  With PD == 2, tile t
-  // waits in register set t & 1; the K loop is unrolled by two so every set
-  // index is a compile-time constant (no indexed register access).
+  // Global loads run PD K steps ahead of the MFMAs: tile t waits in register
+  // set t % PD and is consumed from LDS buffer t & 1; the K loop is unrolled by
+  // max(PD, 2) so every set and buffer index is a compile-time constant (no
+  // indexed register access).
   u32x4 ra[PD][NA], rb[PD][NB];
   // A source rows, resolved once (for the gathered operand: the token's
   // embedding row and the row's draft hidden state, each K/2 wide)
@@ -287,8 +288,6 @@ __global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel
     }
   };
   using C0 = std::integral_constant<int, 0>;
-  using C1 = std::integral_constant<int, 1>;
-  using CS1 = std::integral_constant<int, PD == 2 ? 1 : 0>;
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -318,27 +317,33 @@ __global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel
       }
     }
   };
-  // one K step on LDS buffer B: compute, publish tile kt+1, request tile kt+1+PD
-  auto step = [&](int kt, auto buf_c) {
+  // one K step: compute from LDS buffer kt & 1, publish tile kt+1 (register
+  // set (kt+1) % PD) in the other buffer, request tile kt+1+PD into that set
+  auto step = [&](int kt, auto buf_c, auto setn_c) {
     constexpr int cur = decltype(buf_c)::value;
     using Nxt = std::integral_constant<int, cur ^ 1>;
-    // tile kt+1 lives in set (kt+1) % PD == (cur ^ 1) % PD, tile kt+1+PD reuses it
-    using SetN = std::integral_constant<int, PD == 2 ? (cur ^ 1) : 0>;
     compute(buf_c);
-    if (kt + 1 < nk) stash(Nxt{}, SetN{});
-    if (kt + 1 + PD < nk) fetch(kt + 1 + PD, SetN{});
+    if (kt + 1 < nk) stash(Nxt{}, setn_c);
+    if (kt + 1 + PD < nk) fetch(kt + 1 + PD, setn_c);
     __syncthreads();
   };
 
-  fetch(0, C0{});  // every split has at least one K step (splits <= K / BK)
-  if (PD == 2 && nk > 1) fetch(1, CS1{});
+  // prologue: tiles 0 .. PD-1 requested into sets 0 .. PD-1 (every split has
+  // at least one K step: splits <= K / BK), tile 0 published, tile PD
+  // requested into the set tile 0 freed
+  static_for<PD>([&](auto j_c) {
+    if (decltype(j_c)::value < nk) fetch(decltype(j_c)::value, j_c);
+  });
   stash(C0{}, C0{});
-  if (PD == 1 && nk > 1) fetch(1, C0{});
-  if (PD == 2 && nk > 2) fetch(2, C0{});
+  if (PD < nk) fetch(PD, C0{});
   __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(kt, C0{});
-    if (kt + 1 < nk) step(kt + 1, C1{});
+  constexpr int UN = PD == 1 ? 2 : PD;
+  for (int kt = 0; kt < nk; kt += UN) {
+    static_for<UN>([&](auto j_c) {
+      constexpr int j = decltype(j_c)::value;
+      if (kt + j < nk)
+        step(kt + j, std::integral_constant<int, j & 1>{}, std::integral_constant<int, (j + 1) % PD>{});
+    });
   }
 
   // ---------------------------------------------------------------- epilogue
