@@ -317,34 +317,43 @@ __global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel
       }
     }
   };
-  // one K step: compute from LDS buffer kt & 1, publish tile kt+1 (register
-  // set (kt+1) % PD) in the other buffer, request tile kt+1+PD into that set
+  // One K step: compute from LDS buffer kt & 1, publish tile kt+1 (register
+  // set (kt+1) % PD) in the other buffer, request tile kt+1+PD into that set.
+  // Publishing and requesting are unconditional -- past the last tile they
+  // re-request the last tile (cache hits) and publish into a buffer nobody
+  // reads -- so the steady state has no branches and the compiler's counters
+  // of outstanding loads stay exact: publishing tile kt+1 waits only for its
+  // own loads, with the PD-1 younger tiles still in flight.
   auto step = [&](int kt, auto buf_c, auto setn_c) {
     constexpr int cur = decltype(buf_c)::value;
     using Nxt = std::integral_constant<int, cur ^ 1>;
     compute(buf_c);
-    if (kt + 1 < nk) stash(Nxt{}, setn_c);
-    if (kt + 1 + PD < nk) fetch(kt + 1 + PD, setn_c);
+    stash(Nxt{}, setn_c);
+    fetch(min(kt + 1 + PD, nk - 1), setn_c);
     __syncthreads();
   };
 
-  // prologue: tiles 0 .. PD-1 requested into sets 0 .. PD-1 (every split has
-  // at least one K step: splits <= K / BK), tile 0 published, tile PD
-  // requested into the set tile 0 freed
-  static_for<PD>([&](auto j_c) {
-    if (decltype(j_c)::value < nk) fetch(decltype(j_c)::value, j_c);
-  });
+  // prologue: tiles 0 .. PD-1 requested into sets 0 .. PD-1 (clamped to the
+  // split's last tile; every split has at least one: splits <= K / BK), tile 0
+  // published, tile PD requested into the set tile 0 freed
+  static_for<PD>([&](auto j_c) { fetch(min(static_cast<int>(decltype(j_c)::value), nk - 1), j_c); });
   stash(C0{}, C0{});
-  if (PD < nk) fetch(PD, C0{});
+  fetch(min(PD, nk - 1), C0{});
   __syncthreads();
+  // whole unrolled blocks without branches, then the remaining steps
   constexpr int UN = PD == 1 ? 2 : PD;
-  for (int kt = 0; kt < nk; kt += UN) {
+  const int nk_main = nk - nk % UN;
+  for (int kt = 0; kt < nk_main; kt += UN) {
     static_for<UN>([&](auto j_c) {
       constexpr int j = decltype(j_c)::value;
-      if (kt + j < nk)
-        step(kt + j, std::integral_constant<int, j & 1>{}, std::integral_constant<int, (j + 1) % PD>{});
+      step(kt + j, std::integral_constant<int, j & 1>{}, std::integral_constant<int, (j + 1) % PD>{});
     });
   }
+  static_for<UN - 1>([&](auto j_c) {
+    constexpr int j = decltype(j_c)::value;
+    if (nk_main + j < nk)
+      step(nk_main + j, std::integral_constant<int, j & 1>{}, std::integral_constant<int, (j + 1) % PD>{});
+  });
 
   // ---------------------------------------------------------------- epilogue
   static_assert(WGN * BM * sizeof(Top2) <= sizeof(Bs) / 2, "argmax scratch must fit one LDS buffer");
@@ -352,7 +361,8 @@ __global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel
                                                splits);
 }
 
-// Tile shapes (K step 32 for the 256-column tile, 64 for the others).
+// Tile shapes (K step 32 for the 256-column tile, 64 for the others; loads
+// run two K steps ahead for all three).
 struct TileCfg {
   int bm, bn;
 };
@@ -368,7 +378,8 @@ int tiles_of(const TileCfg& t, int M, int Nout, Epi epi) {
 // several M tiles to share each W tile in L2 and a workgroup per CU, the
 // 128-column tile with two workgroups per CU, else the 64-column tile.
 TileCfg pick_tile(int M, int Nout, Epi epi, int num_cus) {
-  if (M > 128 && tiles_of(kLarge, M, Nout, epi) >= num_cus) return kLarge;
+  // (the q/k/v epilogue does not fit the 256-column tile's registers)
+  if (M > 128 && epi != Epi::QkvRope && tiles_of(kLarge, M, Nout, epi) >= num_cus) return kLarge;
   if (tiles_of(kMedium, M, Nout, epi) >= 2 * num_cus) return kMedium;
   return kSmall;
 }
@@ -408,8 +419,8 @@ hipError_t launch_cfg(GemvArgs& a, int num_cus, hipStream_t s) {
       tiles_of(t, a.M, a.Nout, EPI) < 2 * num_cus)
     t = kMedium;
   if (t.bn == 256) return launch_t<128, 256, 32, 2, 2, EPI, MODE>(a, num_cus, s);
-  if (t.bn == 128) return launch_t<128, 128, 64, 1, 2, EPI, MODE>(a, num_cus, s);
-  return launch_t<128, 64, 64, 1, 2, EPI, MODE>(a, num_cus, s);
+  if (t.bn == 128) return launch_t<128, 128, 64, 2, 2, EPI, MODE>(a, num_cus, s);
+  return launch_t<128, 64, 64, 2, 2, EPI, MODE>(a, num_cus, s);
 }
 
 }  // namespace
