@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel
       ap1[i] = ap0[i];
     }
   }
-  auto fetch = [&](int kt, auto set_c) {
+  auto fetch = [&](int kt, auto set_c) __attribute__((always_inline)) {
     constexpr int set = decltype(set_c)::value;
     const int k0 = (kbase + kt) * BK;
 #pragma unroll
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel
       rb[set][i] = load16(p + k0);
     }
   };
-  auto stash = [&](auto buf_c, auto set_c) {
+  auto stash = [&](auto buf_c, auto set_c) __attribute__((always_inline)) {
     constexpr int buf = decltype(buf_c)::value, set = decltype(set_c)::value;
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel
     for (int jn = 0; jn < TN; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int l16 = lane & 15, lq = lane >> 4;
-  auto compute = [&](auto buf_c) {
+  auto compute = [&](auto buf_c) __attribute__((always_inline)) {
     constexpr int cur = decltype(buf_c)::value;
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel
   // reads -- so the steady state has no branches and the compiler's counters
   // of outstanding loads stay exact: publishing tile kt+1 waits only for its
   // own loads, with the PD-1 younger tiles still in flight.
-  auto step = [&](int kt, auto buf_c, auto setn_c) {
+  auto step = [&](int kt, auto buf_c, auto setn_c) __attribute__((always_inline)) {
     constexpr int cur = decltype(buf_c)::value;
     using Nxt = std::integral_constant<int, cur ^ 1>;
     compute(buf_c);
