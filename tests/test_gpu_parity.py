@@ -171,6 +171,14 @@ def test_forward_two_layer_bf16_mfma_splits():
     _forward_case(wl)
 
 
+def test_forward_qwen_c1_full():
+    """Qwen-shaped drafter at one sequence: 14 rows, so the packed few-row
+    projections with 128-dim heads (q/k/v tiles in pairs, RoPE pairs 64 apart)."""
+    wl = synth.Workload("qwen3coder30b-bf16-c1-k7", synth.QWEN3CODER30B, c=1, K=7, ctx_lo=1024, ctx_hi=3000,
+                        accept_hi=7, seed=81, weight_seed=4)
+    _forward_case(wl)
+
+
 def test_forward_small_bf16():
     spec = synth.ModelSpec(hidden=256, vocab=1000, n_layers=1, n_q=8, n_kv=2, head_dim=64, inter=512)
     wl = synth.Workload("small-bf16", spec, c=6, K=5, ctx_lo=10, ctx_hi=300, accept_hi=5, seed=41)

@@ -61,7 +61,8 @@ def _cache_close(spec, got, want, where, chained=False):
         np.testing.assert_allclose(g[both], w[both], rtol=2.0 ** -7, atol=1e-2, err_msg=where)
 
 
-@pytest.mark.parametrize("name", ["tiny-fp32-c2-k3", "two-layer-fp32", "small-bf16", "gptoss20b-bf16-c1-k7"])
+@pytest.mark.parametrize("name", ["tiny-fp32-c2-k3", "two-layer-fp32", "small-bf16", "gptoss20b-bf16-c1-k7",
+                                  "qwen3coder30b-bf16-c16-k3"])
 def test_autoregressive_matches_oracle(name):
     import drafting_draft_expand_amd as pe
     wl = _workload(name)
