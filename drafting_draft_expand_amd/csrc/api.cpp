@@ -36,6 +36,7 @@ struct pe_model {
   std::vector<pe_layer_weights> layers;
   const void* pk_fc = nullptr;
   std::vector<PackedLayer> pk_layers;  // empty: not packed
+  const void* pk_lm = nullptr;         // tile-major LM head (packed models)
   int num_cus = 0;  // queried on first launch
   pe::RopeFreq freq; // theta^(-2j/d) in double precision
   Timing timing[3];
@@ -265,6 +266,7 @@ size_t pe_packed_weights_bytes(const pe_model* m) {
   std::vector<pe::PackArgs> plan;
   pack_plan(m, plan);
   for (const pe::PackArgs& p : plan) total += align_up(pe::packed_bytes(p.Nout, p.K));
+  if (!plan.empty()) total += align_up(pe::packed_tile_bytes(m->d.vocab, m->d.hidden));
   return total;
 }
 
@@ -283,6 +285,8 @@ pe_status pe_model_pack_weights(pe_model* m, void* packed, size_t packed_bytes, 
     PE_HIP(pe::launch_pack(p, stream));
     b += align_up(pe::packed_bytes(p.Nout, p.K));
   }
+  PE_HIP(pe::launch_pack_tiles(m->w.w_lm, m->d.vocab, m->d.hidden, b, stream));
+  m->pk_lm = b;
   m->pk_fc = dst[0];
   m->pk_layers.assign(m->d.n_layers, PackedLayer{});
   for (int l = 0; l < m->d.n_layers; ++l) {
@@ -589,6 +593,7 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
       g.amode = pe::AMode::Plain; g.x = f;
     }
     g.w_a = g.w_b = g.w_c = m->w.w_lm; g.n_a = d.vocab; g.n_b = 0;
+    g.pk_tiles = m->pk_lm;
     g.logits = logits; g.partials = top2;
     if (pe::gemv_grid_x(S, d.vocab, pe::Epi::Argmax, t, cus, H) > ws.lm_parts) return PE_EUNSUPPORTED;
     {

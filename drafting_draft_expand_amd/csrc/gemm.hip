@@ -21,6 +21,7 @@
 // q/k/v with RoPE and the paged KV write (each 16-column MFMA tile holds 8
 // rotary pairs, columns c and c^8), and LM-head argmax candidates per
 // (row, 256-column tile).
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -361,6 +362,241 @@ __global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel
                                                splits);
 }
 
+// ------------------------------------------------------------- LDS-DMA ring
+// The same tiles fed by direct global -> LDS copies (global_load_lds_dwordx4)
+// into a ring of ST LDS stages, one 32-deep K step each; no register staging.
+// A wave's copy instruction writes one contiguous KiB of LDS, 16 tile rows of
+// 64 bytes, lane l landing in row l / 4, chunk l % 4; the lane fetches the
+// global chunk that the row's XOR swizzle places there, so the fragment reads
+// are the register-staged kernel's.
+//
+// Operand layouts.  Row-major, a copy instruction gathers 16 rows x 64 bytes;
+// tile-major ("packed": [rows / G][K / 32][G][32], G = 256 for W, BM for A,
+// each K step of a row group one contiguous block) it reads one contiguous
+// KiB.  On this GPU the contiguous form keeps the L2 -> LDS path about 10-20%
+// busier for the LM head over 448 rows (measured 0.31-0.33 of bf16 peak
+// row-major, 0.37-0.44 with both operands packed).
+//
+// Synchronisation is explicit (the compiler does not track these LDS
+// writes).  Without fragment prefetch (PF false), step t waits until its own
+// copies of stage t have landed and its LDS reads of step t-1 are done
+// (s_waitcnt with ST-2 stages still in flight), one barrier makes that hold
+// for the whole workgroup, then the wave requests step t+ST-1 into the slot
+// step t-1 used and multiplies.  With PF, the fragments of step t+1 are read
+// from LDS while step t's MFMAs run: at the end of step t the wave waits for
+// stage t+2 and for its reads, and the barrier publishes stage t+2 and frees
+// slot t+1's predecessor; step t then requests step t+ST into slot t, whose
+// fragments are already in registers.  Requests past the split's last step
+// re-read that step (cache hits) so the steady state has no branches.
+
+// 16 bytes per lane from global memory straight into LDS: lane l of the wave
+// writes lds + 16 l (lds wave-uniform).  Issued from inline assembly so that
+// the compiler's own wait-count bookkeeping, which cannot tell ring stages
+// apart and would wait for every copy before the next LDS read, leaves these
+// copies alone: the kernel waits for them itself.  M0 holds the LDS address
+// and needs one wait state before the copy reads it.
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const unsigned m = __builtin_amdgcn_readfirstlane(
+      static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds)));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(m) : "memory", "m0");
+#endif
+}
+
+// s_waitcnt immediate (gfx9 family): at most n vector-memory operations and no
+// LDS / scalar-memory operations outstanding (export count left at its maximum)
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4); }
+
+// Row group of the tile-major W copy (packed_tile_bytes / launch_pack_tiles).
+constexpr int kTileGroup = 256;
+
+template <int BM, int BN, int ST, bool PF, bool PKA, bool PKW, Epi EPI>
+__global__ __launch_bounds__(256, ST * (BM + BN) * 64 > 80 * 1024 ? 1 : 2) void gemm_ring_kernel(GemvArgs a,
+                                                                                              int num_m, int num_n,
+                                                                                              int splits) {
+  constexpr int BK = 32, CPR = 4, WGM = 2, WGN = 2;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int TM = WM / 16, TN = WN / 16;
+  static_assert(EPI == Epi::Argmax || EPI == Epi::Store || EPI == Epi::AddTo, "plain W rows only");
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "whole 16-row copy blocks for every wave");
+  static_assert(!PKW || kTileGroup % BN == 0, "a W tile lies inside one packed row group");
+  constexpr int IA = BM / 64, IB = BN / 64;  // copy instructions per wave and stage
+  constexpr int NI = IA + IB;
+  static_assert(ST >= 3 && (ST - 2) * NI <= 63, "outstanding copy count must fit the counter");
+  static_assert(WGN * BM * sizeof(Top2) <= sizeof(bf16_t) * (BM + BN) * BK, "argmax scratch must fit one ring stage");
+  // One LDS variable per ring stage (A rows then W rows) so every stage is
+  // addressed by a compile-time constant.
+  constexpr int SZ = (BM + BN) * BK;
+  __shared__ __attribute__((aligned(16))) bf16_t R0[SZ];
+  __shared__ __attribute__((aligned(16))) bf16_t R1[SZ];
+  __shared__ __attribute__((aligned(16))) bf16_t R2[SZ];
+  __shared__ __attribute__((aligned(16))) bf16_t R3[ST > 3 ? SZ : 8];
+  __shared__ __attribute__((aligned(16))) bf16_t R4[ST > 4 ? SZ : 8];
+  static_assert(ST <= 5, "at most five ring stages");
+  auto ring = [&](auto s_c) __attribute__((always_inline)) -> bf16_t* {
+    constexpr int S = decltype(s_c)::value % ST;
+    if constexpr (S == 0) return R0;
+    else if constexpr (S == 1) return R1;
+    else if constexpr (S == 2) return R2;
+    else if constexpr (S == 3) return R3;
+    else return R4;
+  };
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % WGM, wn = wave / WGM;
+  const int total = num_m * num_n * splits;
+  const int per_xcd = (total + 7) / 8;
+  const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (L >= total) return;
+  const int mt = L % num_m, rest = L / num_m;
+  const int z = rest % splits, nt = rest / splits;
+  const int m0 = mt * BM;
+  if (a.m_live && m0 >= *a.m_live) return;
+  const int nk_all = a.K / BK;
+  const int per_split = (nk_all + splits - 1) / splits;
+  const int kbase = min(nk_all, z * per_split);
+  const int nk = min(nk_all, kbase + per_split) - kbase;
+
+  // this lane's source chunk in each of the wave's copy blocks, at K step 0,
+  // and the element stride from one K step to the next
+  const int lrow = lane >> 2;
+  const bf16_t* ap[IA];
+#pragma unroll
+  for (int q = 0; q < IA; ++q) {
+    const int r = (q * 4 + wave) * 16 + lrow;
+    const int gc = (lane & 3) ^ ((r >> 1) & 3);
+    if constexpr (PKA)
+      ap[q] = static_cast<const bf16_t*>(a.x) + (static_cast<int64_t>(mt) * nk_all * BM + r) * BK + gc * 8;
+    else
+      ap[q] = static_cast<const bf16_t*>(a.x) + static_cast<int64_t>(min(m0 + r, a.M - 1)) * a.K + gc * 8;
+  }
+  const bf16_t* bp[IB];
+#pragma unroll
+  for (int q = 0; q < IB; ++q) {
+    const int r = (q * 4 + wave) * 16 + lrow;
+    const int gc = (lane & 3) ^ ((r >> 1) & 3);
+    if constexpr (PKW) {
+      const int row = nt * BN + r;  // rows past Nout exist in the packed copy
+      bp[q] = static_cast<const bf16_t*>(a.pk_tiles) +
+              ((static_cast<int64_t>(row / kTileGroup) * nk_all) * kTileGroup + row % kTileGroup) * BK + gc * 8;
+    } else {
+      bp[q] = b_ptr<EPI, BN, WN>(a, nt, r) + gc * 8;
+    }
+  }
+  constexpr int64_t A_STEP = PKA ? BM * BK : BK, B_STEP = PKW ? kTileGroup * BK : BK;
+  auto request = [&](int kt, auto s_c) __attribute__((always_inline)) {
+    bf16_t* st = ring(s_c);
+    const int64_t k = kbase + min(kt, nk - 1);
+#pragma unroll
+    for (int q = 0; q < IA; ++q) dma16(ap[q] + k * A_STEP, st + (q * 4 + wave) * 16 * BK);
+#pragma unroll
+    for (int q = 0; q < IB; ++q) dma16(bp[q] + k * B_STEP, st + BM * BK + (q * 4 + wave) * 16 * BK);
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int jn = 0; jn < TN; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int l16 = lane & 15, lq = lane >> 4;
+  constexpr int NF = PF ? 2 : 1;  // fragment sets
+  u32x4 fa[NF][TM], fb[NF][TN];
+  auto frags = [&](auto s_c, auto f_c) __attribute__((always_inline)) {
+    constexpr int F = decltype(f_c)::value;
+    const bf16_t* as = ring(s_c);
+    const bf16_t* bs = as + BM * BK;
+#pragma unroll
+    for (int jn = 0; jn < TN; ++jn)
+      fb[F][jn] = *reinterpret_cast<const u32x4*>(&bs[lds_off<CPR>(wn * WN + jn * 16 + l16, lq)]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      fa[F][i] = *reinterpret_cast<const u32x4*>(&as[lds_off<CPR>(wm * WM + i * 16 + l16, lq)]);
+  };
+  auto mma = [&](auto f_c) __attribute__((always_inline)) {
+    constexpr int F = decltype(f_c)::value;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int jn = 0; jn < TN; ++jn)
+        acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[F][i]),
+                                                             __builtin_bit_cast(bf16x8, fb[F][jn]), acc[i][jn], 0, 0, 0);
+  };
+  // wait until at most ST-2 stages of copies are in flight and no LDS read
+  // is, then meet the other waves
+  constexpr int kWait = waitcnt_vm_lgkm0((ST - 2) * NI);
+  auto sync = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(kWait);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using C0 = std::integral_constant<int, 0>;
+
+  if constexpr (PF) {
+    // prologue: steps 0 .. ST-1 requested, stages 0 and 1 landed everywhere,
+    // step 0's fragments in registers and every wave done reading slot 0
+    static_for<ST>([&](auto s_c) { request(decltype(s_c)::value, s_c); });
+    sync();
+    frags(C0{}, C0{});
+    sync();
+    auto step = [&](int t, auto j_c) __attribute__((always_inline)) {
+      constexpr int J = decltype(j_c)::value;
+      request(t + ST, std::integral_constant<int, J % ST>{});
+      __builtin_amdgcn_sched_barrier(0);
+      frags(std::integral_constant<int, (J + 1) % ST>{}, std::integral_constant<int, (J + 1) & 1>{});
+      mma(std::integral_constant<int, J & 1>{});
+      // one fragment read, then two MFMAs, ..., then the remaining MFMAs
+      static_for<TM + TN>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      });
+      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - 2 * (TM + TN), 0);
+      sync();
+    };
+    constexpr int U = ST % 2 == 0 ? ST : 2 * ST;
+    int t = 0;
+    for (; t + U <= nk; t += U) static_for<U>([&](auto j_c) { step(t + decltype(j_c)::value, j_c); });
+    static_for<U - 1>([&](auto j_c) {
+      if (t + decltype(j_c)::value < nk) step(t + decltype(j_c)::value, j_c);
+    });
+  } else {
+    static_for<ST - 1>([&](auto s_c) { request(decltype(s_c)::value, s_c); });
+    auto step = [&](int t, auto s_c) __attribute__((always_inline)) {
+      constexpr int S = decltype(s_c)::value;
+      sync();
+      request(t + ST - 1, std::integral_constant<int, (S + ST - 1) % ST>{});
+      frags(s_c, C0{});
+      mma(C0{});
+    };
+    int t = 0;
+    for (; t + ST <= nk; t += ST) static_for<ST>([&](auto s_c) { step(t + decltype(s_c)::value, s_c); });
+    static_for<ST - 1>([&](auto s_c) {
+      if (t + decltype(s_c)::value < nk) step(t + decltype(s_c)::value, s_c);
+    });
+  }
+  // every copy (the clamped requests past the end included) has landed and
+  // every LDS read is done before the epilogue reuses slot 0
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  tile_epilogue<BM, BN, WGM, WGN, TM, TN, EPI>(a, acc, m0, nt, num_n, wm, wn, reinterpret_cast<Top2*>(R0), z, splits);
+}
+
+int gemm_splits(const GemvArgs& a, Epi epi, int tiles, int nk_all, int num_cus);
+
+template <int BM, int BN, int ST, bool PF, bool PKA, bool PKW, Epi EPI>
+hipError_t launch_ring(GemvArgs& a, int num_cus, hipStream_t s) {
+  const int num_m = (a.M + BM - 1) / BM;
+  const int num_n = (a.Nout + BN - 1) / BN;
+  const int splits = gemm_splits(a, EPI, num_m * num_n, a.K / 32, num_cus);
+  const int total = num_m * num_n * splits;
+  const int grid = ((total + 7) / 8) * 8;
+  a.grid_x = num_n;
+  a.splits = splits;
+  hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, ST, PF, PKA, PKW, EPI>), dim3(grid), dim3(256), 0, s, a, num_m, num_n,
+                     splits);
+  return hipGetLastError();
+}
+
 // Tile shapes (K step 32 for the 256-column tile, 64 for the others; loads
 // run two K steps ahead for all three).
 struct TileCfg {
@@ -423,7 +659,39 @@ hipError_t launch_cfg(GemvArgs& a, int num_cus, hipStream_t s) {
   return launch_t<128, 64, 64, 2, 2, EPI, MODE>(a, num_cus, s);
 }
 
+// dst[((g * (K / 32) + kt) * 256 + r) * 32 + c] = W[g * 256 + r][kt * 32 + c],
+// rows past Nout zero; one thread per 16-byte chunk
+__global__ void pack_tiles_kernel(const bf16_t* __restrict__ w, bf16_t* __restrict__ dst, int Nout, int K,
+                                  int64_t chunks) {
+  const int nk = K / 32;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < chunks;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int c = static_cast<int>(i & 3);
+    const int64_t rest = i >> 2;
+    const int r = static_cast<int>(rest % kTileGroup);
+    const int64_t rest2 = rest / kTileGroup;
+    const int kt = static_cast<int>(rest2 % nk);
+    const int64_t row = (rest2 / nk) * kTileGroup + r;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (row < Nout) v = load16(w + row * K + kt * 32 + c * 8);
+    store16(dst + i * 8, v);
+  }
+}
+
 }  // namespace
+
+size_t packed_tile_bytes(int Nout, int K) {
+  return static_cast<size_t>((Nout + kTileGroup - 1) / kTileGroup) * kTileGroup * K * 2;
+}
+
+hipError_t launch_pack_tiles(const void* w, int Nout, int K, void* dst, hipStream_t s) {
+  if (!w || !dst || Nout <= 0 || K <= 0 || K % 32 != 0) return hipErrorInvalidValue;
+  const int64_t chunks = static_cast<int64_t>(packed_tile_bytes(Nout, K) / 16);
+  const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, 16384);
+  hipLaunchKernelGGL(pack_tiles_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(w), static_cast<bf16_t*>(dst), Nout, K, chunks);
+  return hipGetLastError();
+}
 
 int gemm_parts(int M, int Nout, int num_cus) {
   const TileCfg t = pick_tile(M, Nout, Epi::Argmax, num_cus);
@@ -441,7 +709,14 @@ hipError_t launch_gemm(GemvArgs& a, Epi epi, int num_cus, hipStream_t s) {
     case Epi::AddTo: return launch_cfg<Epi::AddTo, AMode::Plain>(a, num_cus, s);
     case Epi::SiluMul: return launch_cfg<Epi::SiluMul, AMode::Plain>(a, num_cus, s);
     case Epi::QkvRope: return launch_cfg<Epi::QkvRope, AMode::Plain>(a, num_cus, s);
-    case Epi::Argmax: return launch_cfg<Epi::Argmax, AMode::Plain>(a, num_cus, s);
+    case Epi::Argmax:
+      // with the tile-major copy: the LDS-DMA ring, 128 x 256 tiles (fragment
+      // prefetch once several M tiles share each W tile)
+      if (a.pk_tiles) {
+        if (a.M > 128) return launch_ring<128, 256, 3, true, false, true, Epi::Argmax>(a, num_cus, s);
+        return launch_ring<128, 256, 3, false, false, true, Epi::Argmax>(a, num_cus, s);
+      }
+      return launch_cfg<Epi::Argmax, AMode::Plain>(a, num_cus, s);
   }
   return hipErrorInvalidValue;
 }

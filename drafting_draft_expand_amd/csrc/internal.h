@@ -99,6 +99,9 @@ struct GemvArgs {
   // the weight-streaming MFMA kernel when set: pk_a for all Nout rows (the gate
   // for SiluMul), pk_b the up projection
   const void *pk_a, *pk_b;
+  // tile-major copy of the rows for the tiled GEMM's argmax epilogue (LM head):
+  // [ceil(Nout / 256)][K / 32][256][32], rows past Nout zero (launch_pack_tiles)
+  const void* pk_tiles;
   // outputs
   float* y;                    // Store / AddTo: fp32 [M, ldy]
   void* y_op;                  // SiluMul: model dtype [M, ldy]
@@ -138,6 +141,10 @@ struct PackArgs {
 };
 size_t packed_bytes(int Nout, int K);
 hipError_t launch_pack(const PackArgs& p, hipStream_t s);
+// Tile-major copy of a row-major bf16 [Nout, K] matrix (K % 32 == 0) in
+// 256-row groups, each 32-deep K step of a group one contiguous 16 KiB block.
+size_t packed_tile_bytes(int Nout, int K);
+hipError_t launch_pack_tiles(const void* w, int Nout, int K, void* dst, hipStream_t s);
 
 // ---------------------------------------------------------------- small kernels
 hipError_t launch_build_fc_input(DType dt, int N, int H, const int32_t* ids, const void* embed,

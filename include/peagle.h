@@ -115,17 +115,20 @@ typedef struct pe_model pe_model; /* opaque; usable from any stream once created
 pe_status pe_model_create(const pe_model_desc *desc, const pe_weights *weights, pe_model **out);
 void pe_model_destroy(pe_model *model);
 
-/* Bytes of device memory for the packed copy of the projection weights (fc and
- * every layer's q/k/v, o, gate, up, down); 0 when the model has nothing to pack
- * (fp32 weights, no layers, or hidden / n_q*head_dim / inter not multiples of
- * 32 or head_dim not a multiple of 16). */
+/* Bytes of device memory for the packed copies of the weights: the projection
+ * weights (fc and every layer's q/k/v, o, gate, up, down) and the LM head
+ * (vocab rounded up to 256 rows x hidden); 0 when the model has nothing to
+ * pack (fp32 weights, no layers, or hidden / n_q*head_dim / inter not
+ * multiples of 32 or head_dim not a multiple of 16). */
 size_t pe_packed_weights_bytes(const pe_model *model);
 
-/* Optional, for speed with few draft rows (at most 16 rows per pass, e.g. one
- * sequence at K <= 8).  Copies the projection weights into `packed` in the
+/* Optional, for speed.  Copies the projection weights into `packed` in the
  * fragment order of the bf16 matrix-core tiles (each 16-output x 32-input
- * fragment one contiguous KiB, the q/k/v rows grouped in rotary pairs) and
- * attaches the buffer to the model; from then on those projections stream it
+ * fragment one contiguous KiB, the q/k/v rows grouped in rotary pairs), read
+ * with few draft rows (at most 16 rows per pass, e.g. one sequence at K <= 8),
+ * and the LM head tile-major (256-row groups, each 32-deep slice of a group one
+ * contiguous 16 KiB block), read when more than 16 rows are sampled; attaches
+ * the buffer to the model.  From then on those products stream the copies
  * instead of the row-major weights (same products, same results up to the
  * summation order of split partial sums).  `packed`: device buffer of at least
  * pe_packed_weights_bytes() bytes, 256-byte aligned, owned by the caller, not

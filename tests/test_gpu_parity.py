@@ -185,6 +185,16 @@ def test_forward_small_bf16():
     _forward_case(wl)
 
 
+@pytest.mark.parametrize("pack", [True, False])
+def test_forward_bf16_many_sampled_rows(pack):
+    """150 sampled rows over a 1000-token vocab: with the tile-major LM-head copy
+    the prefetching ring kernel (two 128-row tiles, the second ragged; the last
+    256-row vocab group mostly padding), else the register-staged GEMM."""
+    spec = synth.ModelSpec(hidden=256, vocab=1000, n_layers=1, n_q=8, n_kv=2, head_dim=64, inter=512)
+    wl = synth.Workload("many-sampled-bf16", spec, c=30, K=5, ctx_lo=10, ctx_hi=200, accept_hi=5, seed=47)
+    _forward_case(wl, pack=pack)
+
+
 def test_forward_gptoss_c1_full():
     _forward_case(synth.WORKLOADS["gptoss20b-bf16-c1-k7"])
 
