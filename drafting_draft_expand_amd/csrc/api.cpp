@@ -90,7 +90,8 @@ Workspace plan_workspace(const pe_model* m, int c, int K, int N) {
   w.attn_part = off; off += align_up(size_t(N) * d.n_q * w.splits * (d.head_dim + 2) * 4);
   w.mlp = off;       off += align_up(size_t(N) * d.inter * eb);
   w.top2 = off;      off += align_up(size_t(S) * w.lm_parts * sizeof(pe::Top2));
-  w.f = off;         off += align_up(size_t(S) * H * eb);
+  // (rounded up to 128 rows: the LM head may read it tile-major in 128-row groups)
+  w.f = off;         off += align_up(size_t((S + 127) / 128 * 128) * H * eb);
   w.ss0 = off;       off += align_up(size_t((H + 15) / 16) * N * 4);
   w.part = off;      off += align_up(part_bytes(d, N));
   w.total = off;
@@ -579,9 +580,12 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
       }
     }
   }
+  // The LM head over many rows streams the tile-major weight copy; the final
+  // RMSNorm then writes its rows tile-major too (128-row groups).
+  const int lm_group = !fnorm && m->pk_lm && pe::proj_kernel(S, H, t) == pe::ProjKernel::Tiled ? 128 : 0;
   if (!fnorm)
     PE_HIP(pe::launch_rmsnorm(t, S, H, sample_idx, x, m->w.ln_f, d.rms_eps, f, stream, nullptr, xpart,
-                              pend_splits, N, pend_acc));
+                              pend_splits, N, pend_acc, lm_group));
   // LM head + argmax over the sampled rows
   {
     pe::GemvArgs g{};
@@ -594,6 +598,7 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
     }
     g.w_a = g.w_b = g.w_c = m->w.w_lm; g.n_a = d.vocab; g.n_b = 0;
     g.pk_tiles = m->pk_lm;
+    g.x_group = lm_group;
     g.logits = logits; g.partials = top2;
     if (pe::gemv_grid_x(S, d.vocab, pe::Epi::Argmax, t, cus, H) > ws.lm_parts) return PE_EUNSUPPORTED;
     {

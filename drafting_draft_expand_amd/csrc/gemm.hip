@@ -712,10 +712,17 @@ hipError_t launch_gemm(GemvArgs& a, Epi epi, int num_cus, hipStream_t s) {
     case Epi::Argmax:
       // with the tile-major copy: the LDS-DMA ring, 128 x 256 tiles (fragment
       // prefetch once several M tiles share each W tile)
+      // (tile-major activations too when the producer wrote them so)
       if (a.pk_tiles) {
+        if (a.x_group == 128) {
+          if (a.M > 128) return launch_ring<128, 256, 3, true, true, true, Epi::Argmax>(a, num_cus, s);
+          return launch_ring<128, 256, 3, false, true, true, Epi::Argmax>(a, num_cus, s);
+        }
+        if (a.x_group != 0) return hipErrorInvalidValue;
         if (a.M > 128) return launch_ring<128, 256, 3, true, false, true, Epi::Argmax>(a, num_cus, s);
         return launch_ring<128, 256, 3, false, false, true, Epi::Argmax>(a, num_cus, s);
       }
+      if (a.x_group != 0) return hipErrorInvalidValue;
       return launch_cfg<Epi::Argmax, AMode::Plain>(a, num_cus, s);
   }
   return hipErrorInvalidValue;

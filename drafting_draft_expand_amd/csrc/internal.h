@@ -102,6 +102,9 @@ struct GemvArgs {
   // tile-major copy of the rows for the tiled GEMM's argmax epilogue (LM head):
   // [ceil(Nout / 256)][K / 32][256][32], rows past Nout zero (launch_pack_tiles)
   const void* pk_tiles;
+  // x tile-major in groups of x_group rows ([M / G][K / 32][G][32], rows past M
+  // present), 0: row-major; only with pk_tiles, and only G = 128
+  int x_group;
   // outputs
   float* y;                    // Store / AddTo: fp32 [M, ldy]
   void* y_op;                  // SiluMul: model dtype [M, ldy]
@@ -152,12 +155,13 @@ hipError_t launch_build_fc_input(DType dt, int N, int H, const int32_t* ids, con
 // out[i] = RMSNorm(x[r]) * gain, r = row_idx ? row_idx[i] : i; H <= kMaxHidden.
 // With nsplit > 0 the row is first completed from split partials and written
 // back: x[r] = (accumulate ? x[r] : 0) + sum_z part[z][r] (z in order; split z
-// starts at part + z * part_rows * H).
+// starts at part + z * part_rows * H).  out_group > 0 (H % 32 == 0) writes out
+// tile-major in groups of out_group rows: [rows / G][H / 32][G][32].
 constexpr int kMaxHidden = 8192;
 hipError_t launch_rmsnorm(DType dt, int rows, int H, const int32_t* row_idx, float* x, const void* gain,
                           float eps, void* out, hipStream_t s, const int32_t* live = nullptr,
                           const float* part = nullptr, int nsplit = 0, int part_rows = 0,
-                          bool accumulate = false);
+                          bool accumulate = false, int out_group = 0);
 
 struct RopeArgs {
   int N, n_q, n_kv, d, block_size;

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_kernel(int H, const int32_t* __r
                                                        float eps, T* __restrict__ out,
                                                        const int32_t* __restrict__ live,
                                                        const float* __restrict__ part, int64_t part_stride,
-                                                       int accumulate) {
+                                                       int accumulate, int out_group) {
   __shared__ float wave_ss[16];
   const int i = blockIdx.x;
   if (live && i >= *live) return;  // padding row of the compacted layout
@@ -73,15 +73,20 @@ __global__ __launch_bounds__(1024) void rmsnorm_kernel(int H, const int32_t* __r
   ss = 0.f;
   for (int w = 0; w < nw; ++w) ss += wave_ss[w];
   const float scale = 1.f / sqrtf(ss / static_cast<float>(H) + eps);
-  T* o = out + static_cast<int64_t>(i) * H;
+  // row-major, or tile-major in groups of out_group rows: element k of row i at
+  // ((i / G) * (H / 32) + k / 32) * G * 32 + (i % G) * 32 + k % 32 (a piece of
+  // four never straddles a 32-wide slice)
+  const int64_t row_base = out_group > 0 ? static_cast<int64_t>(i / out_group) * out_group * H + (i % out_group) * 32
+                                         : static_cast<int64_t>(i) * H;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int v = threadIdx.x + blockDim.x * u;
     if (v >= nv) continue;
     const f32x4 q = keep[u];
+    const int k = 4 * v;
+    T* o = out + row_base + (out_group > 0 ? static_cast<int64_t>(k / 32) * out_group * 32 + k % 32 : k);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      o[4 * v + e] = Elem<T>::from_f32(q[e] * scale * Elem<T>::to_f32(gain[4 * v + e]));
+    for (int e = 0; e < 4; ++e) o[e] = Elem<T>::from_f32(q[e] * scale * Elem<T>::to_f32(gain[k + e]));
   }
 }
 
@@ -200,29 +205,32 @@ hipError_t launch_build_fc_input(DType dt, int N, int H, const int32_t* ids, con
 namespace {
 template <typename T, int NS>
 void launch_rmsnorm_t(int rows, int H, const int32_t* row_idx, float* x, const void* gain, float eps, void* out,
-                      hipStream_t s, const int32_t* live, const float* part, int64_t stride, bool accumulate) {
+                      hipStream_t s, const int32_t* live, const float* part, int64_t stride, bool accumulate,
+                      int out_group) {
   const int nv = H / 4;
   int threads = ((nv + 1) / 2 + 63) / 64 * 64;  // at most two pieces per thread
   if (threads < 64) threads = 64;
   if (nv <= 1024) threads = (nv + 63) / 64 * 64;  // one piece per thread while that fits
   hipLaunchKernelGGL((rmsnorm_kernel<T, NS>), dim3(rows), dim3(threads), 0, s, H, row_idx, x,
-                     static_cast<const T*>(gain), eps, static_cast<T*>(out), live, part, stride, int(accumulate));
+                     static_cast<const T*>(gain), eps, static_cast<T*>(out), live, part, stride, int(accumulate),
+                     out_group);
 }
 
 template <typename T>
 hipError_t launch_rmsnorm_dt(int rows, int H, const int32_t* row_idx, float* x, const void* gain, float eps,
                              void* out, hipStream_t s, const int32_t* live, const float* part, int nsplit,
-                             int64_t stride, bool accumulate) {
+                             int64_t stride, bool accumulate, int out_group) {
+  const int og = out_group;
   switch (nsplit) {
-    case 0: launch_rmsnorm_t<T, 0>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate); break;
-    case 1: launch_rmsnorm_t<T, 1>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate); break;
-    case 2: launch_rmsnorm_t<T, 2>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate); break;
-    case 3: launch_rmsnorm_t<T, 3>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate); break;
-    case 4: launch_rmsnorm_t<T, 4>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate); break;
-    case 5: launch_rmsnorm_t<T, 5>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate); break;
-    case 6: launch_rmsnorm_t<T, 6>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate); break;
-    case 7: launch_rmsnorm_t<T, 7>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate); break;
-    case 8: launch_rmsnorm_t<T, 8>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate); break;
+    case 0: launch_rmsnorm_t<T, 0>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og); break;
+    case 1: launch_rmsnorm_t<T, 1>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og); break;
+    case 2: launch_rmsnorm_t<T, 2>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og); break;
+    case 3: launch_rmsnorm_t<T, 3>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og); break;
+    case 4: launch_rmsnorm_t<T, 4>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og); break;
+    case 5: launch_rmsnorm_t<T, 5>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og); break;
+    case 6: launch_rmsnorm_t<T, 6>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og); break;
+    case 7: launch_rmsnorm_t<T, 7>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og); break;
+    case 8: launch_rmsnorm_t<T, 8>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -231,13 +239,16 @@ hipError_t launch_rmsnorm_dt(int rows, int H, const int32_t* row_idx, float* x, 
 
 hipError_t launch_rmsnorm(DType dt, int rows, int H, const int32_t* row_idx, float* x, const void* gain,
                           float eps, void* out, hipStream_t s, const int32_t* live, const float* part, int nsplit,
-                          int part_rows, bool accumulate) {
+                          int part_rows, bool accumulate, int out_group) {
   if (H % 4 != 0 || H > kMaxHidden || rows <= 0) return hipErrorInvalidValue;
   if (nsplit > 0 && !part) return hipErrorInvalidValue;
+  if (out_group < 0 || (out_group > 0 && H % 32 != 0)) return hipErrorInvalidValue;
   const int64_t stride = static_cast<int64_t>(part_rows) * H;
   if (dt == DType::F32)
-    return launch_rmsnorm_dt<float>(rows, H, row_idx, x, gain, eps, out, s, live, part, nsplit, stride, accumulate);
-  return launch_rmsnorm_dt<bf16_t>(rows, H, row_idx, x, gain, eps, out, s, live, part, nsplit, stride, accumulate);
+    return launch_rmsnorm_dt<float>(rows, H, row_idx, x, gain, eps, out, s, live, part, nsplit, stride, accumulate,
+                                    out_group);
+  return launch_rmsnorm_dt<bf16_t>(rows, H, row_idx, x, gain, eps, out, s, live, part, nsplit, stride, accumulate,
+                                   out_group);
 }
 
 hipError_t launch_rope_kvwrite(const RopeArgs& a, hipStream_t s) {
