@@ -63,7 +63,7 @@ int attention_splits(int c, int n_kv) {
 
 // Workspace carve-up for one forward call.
 struct Workspace {
-  size_t x, act, qkv, q, attn_part, mlp, top2, f, ss0, part, total;
+  size_t x, act, qkv, q, attn_part, mlp, top2, f, ss0, part, rope, total;
   int splits, lm_parts;
 };
 
@@ -94,6 +94,7 @@ Workspace plan_workspace(const pe_model* m, int c, int K, int N) {
   w.f = off;         off += align_up(size_t((S + 127) / 128 * 128) * H * eb);
   w.ss0 = off;       off += align_up(size_t((H + 15) / 16) * N * 4);
   w.part = off;      off += align_up(part_bytes(d, N));
+  w.rope = off;      off += align_up(size_t(N) * (d.head_dim / 2) * 2 * sizeof(float));
   w.total = off;
   return w;
 }
@@ -465,9 +466,16 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
     pend_acc = e == pe::Epi::AddTo;
     return PE_OK;
   };
-  auto norm_x = [&](const void* gain) -> pe_status {
+  // (cos, sin) of every row's rotary angles, written once by the first layer's
+  // input RMSNorm and read by every layer's q/k/v epilogue
+  float2* rope_tab = reinterpret_cast<float2*>(wb + ws.rope);
+  auto norm_x = [&](const void* gain, bool rope_table = false) -> pe_status {
+    pe::RopeTable rt{};
+    if (rope_table) {
+      rt.pos = draft_pos; rt.out = rope_tab; rt.half = d.head_dim / 2; rt.freq = m->freq;
+    }
     PE_HIP(pe::launch_rmsnorm(t, N, H, nullptr, x, gain, d.rms_eps, act, stream, live, xpart, pend_splits, N,
-                              pend_acc));
+                              pend_acc, 0, rope_table ? &rt : nullptr));
     pend_splits = 0;
     return PE_OK;
   };
@@ -489,7 +497,7 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
       const PackedLayer* P = packed ? &m->pk_layers[l] : nullptr;
       // RMSNorm as its own pass (it also completes split partials): forming it
       // inside the projection would make every workgroup re-read the fp32 rows
-      if ((st = norm_x(L.ln1)) != PE_OK) return st;
+      if ((st = norm_x(L.ln1, l == 0)) != PE_OK) return st;
       {
         // q/k/v -> RoPE -> q operand + paged KV write
         pe::GemvArgs g{};
@@ -499,7 +507,7 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
         g.rope.n_q = d.n_q; g.rope.n_kv = d.n_kv; g.rope.d = d.head_dim; g.rope.block_size = d.block_size;
         g.rope.freq = m->freq; g.rope.pos = draft_pos; g.rope.slot = slot_mapping;
         g.rope.rejected = is_rejected; g.rope.q_out = qrot; g.rope.k_cache = k_cache[l];
-        g.rope.v_cache = v_cache[l];
+        g.rope.v_cache = v_cache[l]; g.rope.table = rope_tab;
         if ((st = proj(g, pe::Epi::QkvRope)) != PE_OK) return st;
       }
       if ((st = attention(l)) != PE_OK) return st;

@@ -117,47 +117,81 @@ __device__ __forceinline__ void tile_epilogue(const GemvArgs& a, f32x4 (&acc)[TM
       }
   } else if constexpr (EPI == Epi::QkvRope) {
     const RopeOut& ro = a.rope;
-    const int d = ro.d;
-    // row metadata once per row (rows outer), columns inner
+    const int d = ro.d;  // 16, 32, 64 or 128
+    const int ld = 31 - __builtin_clz(d);
+    const int half = d >> 1;
+    // column facts once (they do not depend on the row): output head and
+    // element of each of this lane's columns
+    int c_head[TN], c_e[TN];
+    bool c_ok[TN];
+#pragma unroll
+    for (int jn = 0; jn < TN; ++jn) {
+      const int n = b_row<EPI, BN, WN>(a, nt, wn * WN + jn * 16 + l16);
+      c_head[jn] = n >> ld;
+      c_e[jn] = n & (d - 1);
+      c_ok[jn] = nt * BN + wn * WN + jn * 16 + l16 < a.Nout;
+    }
+    // Phase 1: rotate the accumulators in place, 16 rows at a time: with no
+    // store in between, each group's table entries are waited for once
+    // (stores count in the same in-order counter as loads, so a table read
+    // issued after a store would have to wait for that store too).
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      float2 tv[4][TN];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int mc = min(m0 + wm * WM + i * 16 + lq * 4 + q, a.M - 1);
+#pragma unroll
+        for (int jn = 0; jn < TN; ++jn)
+          tv[q][jn] = ro.table[static_cast<int64_t>(mc) * half + (c_e[jn] & (half - 1))];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int jn = 0; jn < TN; ++jn) {
+          const float v = acc[i][jn][q];
+          const float partner = __shfl_xor(v, 8, 64);
+          if (c_head[jn] < ro.n_q + ro.n_kv)
+            acc[i][jn][q] = (l16 & 8) == 0 ? v * tv[q][jn].x - partner * tv[q][jn].y
+                                            : v * tv[q][jn].x + partner * tv[q][jn].y;
+        }
+    }
+    // Phase 2: stores.  Row facts (rejected flag, cache slot) requested in one
+    // batch at clamped rows.
+    uint8_t r_rej[TM * 4];
+    int64_t r_slot[TM * 4];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int mc = min(m0 + wm * WM + i * 16 + lq * 4 + q, a.M - 1);
+        r_rej[i * 4 + q] = ro.rejected[mc];
+        r_slot[i * 4 + q] = ro.slot[mc];
+      }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int m = m0 + wm * WM + i * 16 + lq * 4 + q;
-        const int mc = min(m, a.M - 1);
-        const bool live = m < a.M && !ro.rejected[mc];
-        const int pos = ro.pos[mc];
-        const int64_t slot = ro.slot[mc];
+        if (m >= a.M || r_rej[i * 4 + q]) continue;
+        const int64_t slot = r_slot[i * 4 + q];
+        // 16-token pages (the only page size the library accepts)
+        const int64_t page_row = slot < 0 ? 0 : ((slot >> 4) * ro.n_kv * 16 + (slot & 15)) << ld;
 #pragma unroll
         for (int jn = 0; jn < TN; ++jn) {
-          const int col = nt * BN + wn * WN + jn * 16 + l16;
-          const int n = b_row<EPI, BN, WN>(a, nt, wn * WN + jn * 16 + l16);
-          const int head = n / d;
-          const int e = n - head * d;
-          const bool rotate = head < ro.n_q + ro.n_kv;
-          const float v = acc[i][jn][q];
-          const float partner = __shfl_xor(v, 8, 64);
-          if (!live || col >= a.Nout) continue;
-          float out = v;
-          if (rotate) {
-            float cs, sn;
-            rope_cos_sin(pos, ro.freq.inv[e % (d / 2)], cs, sn);
-            out = (l16 & 8) == 0 ? v * cs - partner * sn : v * cs + partner * sn;
-          }
+          if (!c_ok[jn]) continue;
+          const int head = c_head[jn], e = c_e[jn];
+          const bf16_t out = f32_to_bf16(acc[i][jn][q]);
           if (head < ro.n_q) {
-            static_cast<bf16_t*>(ro.q_out)[(static_cast<int64_t>(m) * ro.n_q + head) * d + e] = f32_to_bf16(out);
-          } else {
-            if (slot < 0) continue;
+            static_cast<bf16_t*>(ro.q_out)[((static_cast<int64_t>(m) * ro.n_q + head) << ld) + e] = out;
+          } else if (slot >= 0) {
             const bool is_k = head < ro.n_q + ro.n_kv;
             const int g = is_k ? head - ro.n_q : head - ro.n_q - ro.n_kv;
-            // 16-token pages (the only page size the library accepts)
-            const int64_t blk = slot >> 4;
-            const int off = static_cast<int>(slot & 15);
-            static_cast<bf16_t*>(is_k ? ro.k_cache : ro.v_cache)[((blk * ro.n_kv + g) * 16 + off) * d + e] =
-                f32_to_bf16(out);
+            static_cast<bf16_t*>(is_k ? ro.k_cache : ro.v_cache)[page_row + (static_cast<int64_t>(g) << (4 + ld)) + e] =
+                out;
           }
         }
-    }
+      }
   } else {  // Argmax over this tile's BN columns, per row
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -417,7 +451,8 @@ __global__ __launch_bounds__(256, ST * (BM + BN) * 64 > 80 * 1024 ? 1 : 2) void 
   constexpr int BK = 32, CPR = 4, WGM = 2, WGN = 2;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 16, TN = WN / 16;
-  static_assert(EPI == Epi::Argmax || EPI == Epi::Store || EPI == Epi::AddTo, "plain W rows only");
+  static_assert(!PKW || EPI == Epi::Argmax || EPI == Epi::Store || EPI == Epi::AddTo,
+                "the tile-major copy holds W rows in plain order");
   static_assert(BM % 64 == 0 && BN % 64 == 0, "whole 16-row copy blocks for every wave");
   static_assert(!PKW || kTileGroup % BN == 0, "a W tile lies inside one packed row group");
   constexpr int IA = BM / 64, IB = BN / 64;  // copy instructions per wave and stage
@@ -586,7 +621,8 @@ int gemm_splits(const GemvArgs& a, Epi epi, int tiles, int nk_all, int num_cus);
 template <int BM, int BN, int ST, bool PF, bool PKA, bool PKW, Epi EPI>
 hipError_t launch_ring(GemvArgs& a, int num_cus, hipStream_t s) {
   const int num_m = (a.M + BM - 1) / BM;
-  const int num_n = (a.Nout + BN - 1) / BN;
+  const int cols = EPI == Epi::SiluMul ? BN / 2 : BN;  // gate + up rows per output column
+  const int num_n = (a.Nout + cols - 1) / cols;
   const int splits = gemm_splits(a, EPI, num_m * num_n, a.K / 32, num_cus);
   const int total = num_m * num_n * splits;
   const int grid = ((total + 7) / 8) * 8;
@@ -621,12 +657,13 @@ TileCfg pick_tile(int M, int Nout, Epi epi, int num_cus) {
 }
 
 // K splits for Store / AddTo when the tiles alone leave CUs idle and the
-// caller takes partial sums: enough for about two workgroups per CU, at most
-// kMaxSplits and at least 8 K steps per split.
+// caller takes partial sums: as many as fit in one round of two workgroups
+// per CU (a few more would start a second, nearly empty round: 552 units over
+// 512 slots ran 10-15% slower than 414), at most kMaxSplits and at least 8 K
+// steps per split.
 int gemm_splits(const GemvArgs& a, Epi epi, int tiles, int nk_all, int num_cus) {
   if (!a.part || a.ss_out || (epi != Epi::Store && epi != Epi::AddTo)) return 1;
-  if (tiles >= 2 * num_cus) return 1;
-  int sp = (2 * num_cus + tiles - 1) / tiles;
+  int sp = 2 * num_cus / tiles;
   if (sp > kMaxSplits) sp = kMaxSplits;
   if (sp > nk_all / 8) sp = nk_all / 8;
   return sp < 2 ? 1 : sp;
@@ -649,6 +686,21 @@ hipError_t launch_t(GemvArgs& a, int num_cus, hipStream_t s) {
 
 template <Epi EPI, AMode MODE>
 hipError_t launch_cfg(GemvArgs& a, int num_cus, hipStream_t s) {
+  // Many rows (more than two 128-row tiles) on a plain operand: the LDS-DMA
+  // ring on row-major W -- 128 x 256 tiles (K split when the caller takes
+  // partials), 128 x 128 for q/k/v (the rotary epilogue spills on the wider
+  // tile).  At 672 rows it ran the o / down / gate-up / q-k-v projections
+  // 7-18% faster than the register-staged tiles.
+  if constexpr (MODE == AMode::Plain && EPI != Epi::Argmax) {
+    if (a.M > 256 && !a.ss_out) {
+      if constexpr (EPI == Epi::QkvRope)
+        return launch_ring<128, 128, 4, false, false, false, EPI>(a, num_cus, s);
+      else if constexpr (EPI == Epi::SiluMul)
+        return launch_ring<128, 256, 3, false, false, false, EPI>(a, num_cus, s);
+      else if (a.part)
+        return launch_ring<128, 256, 3, false, false, false, EPI>(a, num_cus, s);
+    }
+  }
   TileCfg t = pick_tile(a.M, a.Nout, EPI, num_cus);
   // Store / AddTo into split partials: 128 x 128 tiles, K split to fill the CUs
   if ((EPI == Epi::Store || EPI == Epi::AddTo) && a.part && !a.ss_out &&
@@ -699,6 +751,7 @@ int gemm_parts(int M, int Nout, int num_cus) {
 }
 
 hipError_t launch_gemm(GemvArgs& a, Epi epi, int num_cus, hipStream_t s) {
+  if (epi == Epi::QkvRope && !a.rope.table) return hipErrorInvalidValue;
   if (a.amode == AMode::Gather) {
     if (epi == Epi::Store) return launch_cfg<Epi::Store, AMode::Gather>(a, num_cus, s);
     return hipErrorInvalidValue;

@@ -277,9 +277,8 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
   const float inv = (MODE == AMode::Norm && xvalid) ? inv_s[lane & 15] : 0.f;
   const int T = (a.Nout + 15) / 16;
   const int G = (T + NT - 1) / NT;
-  // q/k/v epilogue: the position, rejected flag and cache slot of this lane's
+  // q/k/v epilogue: the rejected flag and cache slot of this lane's
   // four output rows are read once, before the weights stream
-  int r_pos[4] = {0, 0, 0, 0};
   int64_t r_slot[4] = {-1, -1, -1, -1};
   bool r_live[4] = {false, false, false, false};
   if constexpr (EPI == Epi::QkvRope) {
@@ -288,7 +287,6 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
       const int m = 4 * j + q;
       if (m < a.M) {
         r_live[q] = !a.rope.rejected[m];
-        r_pos[q] = a.rope.pos[m];
         r_slot[q] = a.rope.slot[m];
       }
     }
@@ -450,7 +448,6 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
         const int e = n - head * d;                  // element within the head
         const int jj = e % (d / 2);                  // rotary pair index
         const bool rotate = head < ro.n_q + ro.n_kv;
-        const double inv_freq = ro.freq.inv[jj];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int m = 4 * j + q;
@@ -459,9 +456,8 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
           if (!r_live[q]) continue;
           float out = v;
           if (rotate) {
-            float cs, sn;
-            rope_cos_sin(r_pos[q], inv_freq, cs, sn);
-            out = c < 8 ? v * cs - partner * sn : v * cs + partner * sn;
+            const float2 t = ro.table[static_cast<int64_t>(m) * (d / 2) + jj];
+            out = c < 8 ? v * t.x - partner * t.y : v * t.x + partner * t.y;
           }
           if (head < ro.n_q) {
             static_cast<bf16_t*>(ro.q_out)[(static_cast<int64_t>(m) * ro.n_q + head) * d + e] = f32_to_bf16(out);
@@ -698,6 +694,7 @@ size_t gemv_lds_bytes(int M, int K, DType dt) {
 // on the MFMA kernel, Argmax+Norm on the LDS kernel.
 hipError_t launch_gemv(GemvArgs& a, Epi epi, DType dt, int num_cus, hipStream_t s) {
   a.splits = 1;
+  if (epi == Epi::QkvRope && !a.rope.table) return hipErrorInvalidValue;
   if (proj_kernel(a.M, a.K, dt) == ProjKernel::Tiled) return launch_gemm(a, epi, num_cus, s);
   if (use_mfma(a.M, a.K, dt)) {
     if (a.amode == AMode::Plain) {

@@ -72,6 +72,18 @@ struct RopeOut {
   const uint8_t* rejected;
   void* q_out;                 // [M, n_q * d] model dtype
   void *k_cache, *v_cache;     // [blocks, n_kv, block_size, d]
+  // [M][d / 2] (cos, sin) of pos[m] * freq.inv[j] as rope_cos_sin gives them
+  // (written by the RMSNorm before the projection); required
+  const float2* table;
+};
+
+// Rotary table written by launch_rmsnorm: out[i][j] = (cos, sin) of
+// pos[i] * freq.inv[j], j < half, for every row i (padding rows included).
+struct RopeTable {
+  const int32_t* pos;
+  float2* out;
+  int half;
+  RopeFreq freq;
 };
 
 struct GemvArgs {
@@ -161,7 +173,7 @@ constexpr int kMaxHidden = 8192;
 hipError_t launch_rmsnorm(DType dt, int rows, int H, const int32_t* row_idx, float* x, const void* gain,
                           float eps, void* out, hipStream_t s, const int32_t* live = nullptr,
                           const float* part = nullptr, int nsplit = 0, int part_rows = 0,
-                          bool accumulate = false, int out_group = 0);
+                          bool accumulate = false, int out_group = 0, const RopeTable* rope = nullptr);
 
 struct RopeArgs {
   int N, n_q, n_kv, d, block_size;

@@ -34,9 +34,14 @@ __global__ __launch_bounds__(1024) void rmsnorm_kernel(int H, const int32_t* __r
                                                        float eps, T* __restrict__ out,
                                                        const int32_t* __restrict__ live,
                                                        const float* __restrict__ part, int64_t part_stride,
-                                                       int accumulate, int out_group) {
+                                                       int accumulate, int out_group, RopeTable rt) {
   __shared__ float wave_ss[16];
   const int i = blockIdx.x;
+  if (rt.out && static_cast<int>(threadIdx.x) < rt.half) {
+    float c, s;
+    rope_cos_sin(rt.pos[i], rt.freq.inv[threadIdx.x], c, s);
+    rt.out[static_cast<int64_t>(i) * rt.half + threadIdx.x] = make_float2(c, s);
+  }
   if (live && i >= *live) return;  // padding row of the compacted layout
   const int r = row_idx ? row_idx[i] : i;
   f32x4* xr = reinterpret_cast<f32x4*>(x + static_cast<int64_t>(r) * H);
@@ -206,31 +211,32 @@ namespace {
 template <typename T, int NS>
 void launch_rmsnorm_t(int rows, int H, const int32_t* row_idx, float* x, const void* gain, float eps, void* out,
                       hipStream_t s, const int32_t* live, const float* part, int64_t stride, bool accumulate,
-                      int out_group) {
+                      int out_group, const RopeTable& rt) {
   const int nv = H / 4;
   int threads = ((nv + 1) / 2 + 63) / 64 * 64;  // at most two pieces per thread
   if (threads < 64) threads = 64;
   if (nv <= 1024) threads = (nv + 63) / 64 * 64;  // one piece per thread while that fits
+  if (threads < rt.half) threads = (rt.half + 63) / 64 * 64;
   hipLaunchKernelGGL((rmsnorm_kernel<T, NS>), dim3(rows), dim3(threads), 0, s, H, row_idx, x,
                      static_cast<const T*>(gain), eps, static_cast<T*>(out), live, part, stride, int(accumulate),
-                     out_group);
+                     out_group, rt);
 }
 
 template <typename T>
 hipError_t launch_rmsnorm_dt(int rows, int H, const int32_t* row_idx, float* x, const void* gain, float eps,
                              void* out, hipStream_t s, const int32_t* live, const float* part, int nsplit,
-                             int64_t stride, bool accumulate, int out_group) {
+                             int64_t stride, bool accumulate, int out_group, const RopeTable& rt) {
   const int og = out_group;
   switch (nsplit) {
-    case 0: launch_rmsnorm_t<T, 0>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og); break;
-    case 1: launch_rmsnorm_t<T, 1>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og); break;
-    case 2: launch_rmsnorm_t<T, 2>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og); break;
-    case 3: launch_rmsnorm_t<T, 3>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og); break;
-    case 4: launch_rmsnorm_t<T, 4>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og); break;
-    case 5: launch_rmsnorm_t<T, 5>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og); break;
-    case 6: launch_rmsnorm_t<T, 6>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og); break;
-    case 7: launch_rmsnorm_t<T, 7>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og); break;
-    case 8: launch_rmsnorm_t<T, 8>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og); break;
+    case 0: launch_rmsnorm_t<T, 0>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og, rt); break;
+    case 1: launch_rmsnorm_t<T, 1>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og, rt); break;
+    case 2: launch_rmsnorm_t<T, 2>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og, rt); break;
+    case 3: launch_rmsnorm_t<T, 3>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og, rt); break;
+    case 4: launch_rmsnorm_t<T, 4>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og, rt); break;
+    case 5: launch_rmsnorm_t<T, 5>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og, rt); break;
+    case 6: launch_rmsnorm_t<T, 6>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og, rt); break;
+    case 7: launch_rmsnorm_t<T, 7>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og, rt); break;
+    case 8: launch_rmsnorm_t<T, 8>(rows, H, row_idx, x, gain, eps, out, s, live, part, stride, accumulate, og, rt); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -239,16 +245,21 @@ hipError_t launch_rmsnorm_dt(int rows, int H, const int32_t* row_idx, float* x, 
 
 hipError_t launch_rmsnorm(DType dt, int rows, int H, const int32_t* row_idx, float* x, const void* gain,
                           float eps, void* out, hipStream_t s, const int32_t* live, const float* part, int nsplit,
-                          int part_rows, bool accumulate, int out_group) {
+                          int part_rows, bool accumulate, int out_group, const RopeTable* rope) {
   if (H % 4 != 0 || H > kMaxHidden || rows <= 0) return hipErrorInvalidValue;
   if (nsplit > 0 && !part) return hipErrorInvalidValue;
   if (out_group < 0 || (out_group > 0 && H % 32 != 0)) return hipErrorInvalidValue;
+  RopeTable rt{};
+  if (rope && rope->out) {
+    if (rope->half < 1 || rope->half > 64 || !rope->pos) return hipErrorInvalidValue;
+    rt = *rope;
+  }
   const int64_t stride = static_cast<int64_t>(part_rows) * H;
   if (dt == DType::F32)
     return launch_rmsnorm_dt<float>(rows, H, row_idx, x, gain, eps, out, s, live, part, nsplit, stride, accumulate,
-                                    out_group);
+                                    out_group, rt);
   return launch_rmsnorm_dt<bf16_t>(rows, H, row_idx, x, gain, eps, out, s, live, part, nsplit, stride, accumulate,
-                                   out_group);
+                                   out_group, rt);
 }
 
 hipError_t launch_rope_kvwrite(const RopeArgs& a, hipStream_t s) {

@@ -187,12 +187,24 @@ def test_forward_small_bf16():
 
 @pytest.mark.parametrize("pack", [True, False])
 def test_forward_bf16_many_sampled_rows(pack):
-    """150 sampled rows over a 1000-token vocab: with the tile-major LM-head copy
+    """200 sampled rows over a 1000-token vocab: with the tile-major LM-head copy
     the prefetching ring kernel (two 128-row tiles, the second ragged; the last
-    256-row vocab group mostly padding), else the register-staged GEMM."""
+    256-row vocab group mostly padding), else the register-staged GEMM.  About
+    300 draft rows, so the layer projections run the ring kernel on row-major
+    weights (K split for the residual-writing ones)."""
     spec = synth.ModelSpec(hidden=256, vocab=1000, n_layers=1, n_q=8, n_kv=2, head_dim=64, inter=512)
-    wl = synth.Workload("many-sampled-bf16", spec, c=30, K=5, ctx_lo=10, ctx_hi=200, accept_hi=5, seed=47)
+    wl = synth.Workload("many-sampled-bf16", spec, c=40, K=5, ctx_lo=10, ctx_hi=200, accept_hi=5, seed=47)
     _forward_case(wl, pack=pack)
+
+
+def test_forward_bf16_many_rows_ragged():
+    """About 300 draft rows on a drafter whose widths are not multiples of the
+    ring kernel's tiles: hidden 320 (two 256-column tiles, the second ragged),
+    q/k/v 448 columns in 128-column tiles, gate/up 448 outputs in 128-column
+    tiles, ragged last 128-row tile."""
+    spec = synth.ModelSpec(hidden=320, vocab=700, n_layers=1, n_q=5, n_kv=1, head_dim=64, inter=448)
+    wl = synth.Workload("many-rows-ragged-bf16", spec, c=40, K=5, ctx_lo=10, ctx_hi=150, accept_hi=5, seed=48)
+    _forward_case(wl)
 
 
 def test_forward_gptoss_c1_full():
