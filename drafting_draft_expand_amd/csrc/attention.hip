@@ -384,44 +384,52 @@ __global__ __launch_bounds__(512, OCC) void attn_mfma_kernel(AttnArgs a) {
 // first use: lane s reads the statistics of split s, and every lane reads its
 // output dims (lane, lane + 64) of all splits, splits past S clamped to the
 // last one and weighted 0, so the kernel waits for memory once.
-template <typename T, int D>
-__global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
+template <typename T, int D, int MAXS, int HPW>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   constexpr int DV = (D + 63) / 64;  // output dims per lane
-  const int row = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-  const int S = a.splits;
-  T* out = static_cast<T*>(a.out) + (static_cast<int64_t>(row) * a.n_q + h) * D;
-  if (a.rejected[row]) {
-    for (int dd = lane; dd < D; dd += 64) out[dd] = Elem<T>::from_f32(0.f);
-    return;
+  const int row = blockIdx.x, lane = threadIdx.x & 63;
+  const int h0 = (blockIdx.y * 4 + (threadIdx.x >> 6)) * HPW;  // this wave's first head
+  const int S = a.splits;                                      // 1 <= S <= MAXS
+  const bool rejected = a.rejected[row];
+  // HPW heads per wave, unrolled so that their loads are in flight together
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const int h = h0 + hh;
+    if (h >= a.n_q) break;
+    T* out = static_cast<T*>(a.out) + (static_cast<int64_t>(row) * a.n_q + h) * D;
+    if (rejected) {
+      for (int dd = lane; dd < D; dd += 64) out[dd] = Elem<T>::from_f32(0.f);
+      continue;
+    }
+    const float* p = a.partial + (static_cast<int64_t>(row) * a.n_q + h) * S * (D + 2);
+    const int sl = min(lane, S - 1);
+    const float m_l = p[sl * (D + 2) + D];
+    const float l_l = p[sl * (D + 2) + D + 1];
+    float v[DV][MAXS];
+#pragma unroll
+    for (int z = 0; z < MAXS; ++z) {
+      const int zc = min(z, S - 1);
+#pragma unroll
+      for (int e = 0; e < DV; ++e) v[e][z] = p[zc * (D + 2) + min(lane + 64 * e, D - 1)];
+    }
+    const float ms = lane < S ? m_l : -INFINITY;
+    const float M = wave_max(ms);
+    const float w = ms == -INFINITY ? 0.f : expf(ms - M);
+    const float den = wave_sum(lane < S ? w * l_l : 0.f);
+    float num[DV];
+#pragma unroll
+    for (int e = 0; e < DV; ++e) num[e] = 0.f;
+#pragma unroll
+    for (int z = 0; z < MAXS; ++z) {
+      const float wz = __shfl(w, z, 64);  // 0 for splits past S
+#pragma unroll
+      for (int e = 0; e < DV; ++e) num[e] = fmaf(v[e][z], wz, num[e]);
+    }
+    const float inv = 1.f / den;
+#pragma unroll
+    for (int e = 0; e < DV; ++e)
+      if (lane + 64 * e < D) out[lane + 64 * e] = Elem<T>::from_f32(num[e] * inv);
   }
-  const float* p = a.partial + (static_cast<int64_t>(row) * a.n_q + h) * S * (D + 2);
-  const int sl = min(lane, S - 1);
-  const float m_l = p[sl * (D + 2) + D];
-  const float l_l = p[sl * (D + 2) + D + 1];
-  float v[DV][kAttnMaxSplits];
-#pragma unroll
-  for (int z = 0; z < kAttnMaxSplits; ++z) {
-    const int zc = min(z, S - 1);
-#pragma unroll
-    for (int e = 0; e < DV; ++e) v[e][z] = p[zc * (D + 2) + min(lane + 64 * e, D - 1)];
-  }
-  const float ms = lane < S ? m_l : -INFINITY;
-  const float M = wave_max(ms);
-  const float w = ms == -INFINITY ? 0.f : expf(ms - M);
-  const float den = wave_sum(lane < S ? w * l_l : 0.f);
-  float num[DV];
-#pragma unroll
-  for (int e = 0; e < DV; ++e) num[e] = 0.f;
-#pragma unroll
-  for (int z = 0; z < kAttnMaxSplits; ++z) {
-    const float wz = __shfl(w, z, 64);  // 0 for splits past S
-#pragma unroll
-    for (int e = 0; e < DV; ++e) num[e] = fmaf(v[e][z], wz, num[e]);
-  }
-  const float inv = 1.f / den;
-#pragma unroll
-  for (int e = 0; e < DV; ++e)
-    if (lane + 64 * e < D) out[lane + 64 * e] = Elem<T>::from_f32(num[e] * inv);
 }
 
 template <int D>
@@ -433,6 +441,23 @@ void launch_mfma(const AttnArgs& a, dim3 grid, hipStream_t s) {
     hipLaunchKernelGGL((attn_mfma_kernel<D, DEPTH, OCC, true>), grid, dim3(512), 0, s, a);
   else
     hipLaunchKernelGGL((attn_mfma_kernel<D, DEPTH, OCC, false>), grid, dim3(512), 0, s, a);
+}
+
+// Split merge: four waves per workgroup, HPW heads per wave, split loads
+// bounded by the next power of two at or above the split count.
+template <typename T, int D, int MAXS>
+void launch_combine_s(const AttnArgs& a, hipStream_t s) {
+  constexpr int HPW = 2;
+  const dim3 grid(a.N, (a.n_q + 4 * HPW - 1) / (4 * HPW));
+  hipLaunchKernelGGL((attn_combine_kernel<T, D, MAXS, HPW>), grid, dim3(256), 0, s, a);
+}
+template <typename T, int D>
+void launch_combine(const AttnArgs& a, hipStream_t s) {
+  if (a.splits <= 1) launch_combine_s<T, D, 1>(a, s);
+  else if (a.splits <= 2) launch_combine_s<T, D, 2>(a, s);
+  else if (a.splits <= 4) launch_combine_s<T, D, 4>(a, s);
+  else if (a.splits <= 8) launch_combine_s<T, D, 8>(a, s);
+  else launch_combine_s<T, D, kAttnMaxSplits>(a, s);
 }
 
 template <typename T>
@@ -454,12 +479,11 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 cgrid(a.N, a.n_q);
   switch (a.d) {
-    case 16: hipLaunchKernelGGL((attn_combine_kernel<T, 16>), cgrid, dim3(64), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((attn_combine_kernel<T, 32>), cgrid, dim3(64), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((attn_combine_kernel<T, 64>), cgrid, dim3(64), 0, s, a); break;
-    default: hipLaunchKernelGGL((attn_combine_kernel<T, 128>), cgrid, dim3(64), 0, s, a); break;
+    case 16: launch_combine<T, 16>(a, s); break;
+    case 32: launch_combine<T, 32>(a, s); break;
+    case 64: launch_combine<T, 64>(a, s); break;
+    default: launch_combine<T, 128>(a, s); break;
   }
   return hipGetLastError();
 }
