@@ -657,13 +657,16 @@ TileCfg pick_tile(int M, int Nout, Epi epi, int num_cus) {
 }
 
 // K splits for Store / AddTo when the tiles alone leave CUs idle and the
-// caller takes partial sums: as many as fit in one round of two workgroups
-// per CU (a few more would start a second, nearly empty round: 552 units over
-// 512 slots ran 10-15% slower than 414), at most kMaxSplits and at least 8 K
-// steps per split.
+// caller takes partial sums.  One workgroup per CU when that still splits K at
+// least twice, else as many as fit in one round of two per CU: what matters is
+// the busiest CU's share, and a count just past a round boundary doubles it
+// (552 units over 512 slots ran 10-15% slower than 414).  Fewer splits also
+// leave fewer partial sums for the next RMSNorm to read (at 672 rows, 3
+// splits instead of 7 for o / down: the same GEMM time, 2.4 us less per norm).
+// At most kMaxSplits and at least 8 K steps per split.
 int gemm_splits(const GemvArgs& a, Epi epi, int tiles, int nk_all, int num_cus) {
   if (!a.part || a.ss_out || (epi != Epi::Store && epi != Epi::AddTo)) return 1;
-  int sp = 2 * num_cus / tiles;
+  int sp = num_cus / tiles >= 2 ? num_cus / tiles : 2 * num_cus / tiles;
   if (sp > kMaxSplits) sp = kMaxSplits;
   if (sp > nk_all / 8) sp = nk_all / 8;
   return sp < 2 ? 1 : sp;
