@@ -384,6 +384,218 @@ __global__ __launch_bounds__(512, OCC) void attn_mfma_kernel(AttnArgs a) {
 // first use: lane s reads the statistics of split s, and every lane reads its
 // output dims (lane, lane + 64) of all splits, splits past S clamped to the
 // last one and weighted 0, so the kernel waits for memory once.
+// bf16, 64-dim heads, a split's page numbers in LDS: the same products with
+// K and V copied straight into a ring of ST LDS stages (global_load_lds, no
+// register staging), so the copies of later tiles run while the waves compute
+// instead of between their products.  A stage holds the tile's 64 K rows then
+// its 64 V rows, 128 bytes each, unpadded, 16-byte chunk c of key row r at
+// slot c ^ (r & 7): the score-fragment reads (16 rows x 4 chunks) and the
+// transposing V reads both spread over the banks.  Wave w copies keys
+// 8w..8w+7 of K and of V (one KiB each; eight keys never straddle a 16-token
+// page).  Step t waits until its own copies of stage t have landed (ST-2
+// stages still in flight), meets the other waves, requests tile t+ST-1 into
+// the slot step t-1 used, then computes.
+template <int ST>
+__global__ __launch_bounds__(512, 4) void attn_ring_kernel(AttnArgs a) {
+  constexpr int D = 64, KT = 64;
+  constexpr int DT = D / 16, KK = D / 32;
+  constexpr int SK = KT * D;  // elements of one K (or V) tile
+  constexpr int BS = 16;      // KV page size (the only one the library accepts)
+  static_assert(ST >= 3 && ST <= 4, "three or four ring stages");
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(16))) bf16_t R0[2 * SK];
+  __shared__ __attribute__((aligned(16))) bf16_t R1[2 * SK];
+  __shared__ __attribute__((aligned(16))) bf16_t R2[2 * SK];
+  __shared__ __attribute__((aligned(16))) bf16_t R3[ST > 3 ? 2 * SK : 8];
+  __shared__ int32_t pages[kAttnMaxPages];
+  auto ring = [&](auto s_c) __attribute__((always_inline)) -> bf16_t* {
+    constexpr int S = decltype(s_c)::value % ST;
+    if constexpr (S == 0) return R0;
+    else if constexpr (S == 1) return R1;
+    else if constexpr (S == 2) return R2;
+    else return R3;
+  };
+  const int tid = threadIdx.x, lane = tid & 63, j = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sp = blockIdx.x, g = blockIdx.y, i = blockIdx.z;
+  const int grp = a.n_q / a.n_kv;
+  const int r0 = a.cu_draft[i], r1 = a.cu_draft[i + 1];
+  const int kvlen = a.kv_lens[i];
+  const int chunk = ((kvlen + a.splits - 1) / a.splits + KT - 1) / KT * KT;
+  const int kb = sp * chunk;
+  const int ke = min(kvlen, kb + chunk);
+  const int ntiles = ke > kb ? (ke - kb + KT - 1) / KT : 0;
+  const int nqry = (r1 - r0) * grp;
+  const float sl2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));  // scale * log2(e)
+  const bf16_t* qin = static_cast<const bf16_t*>(a.q);
+  const bf16_t* kc = static_cast<const bf16_t*>(a.k_cache);
+  const bf16_t* vc = static_cast<const bf16_t*>(a.v_cache);
+  const int32_t* bt = a.block_table + static_cast<int64_t>(i) * a.max_blocks;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const int pg0 = kb / BS;
+  const int npg = ke > kb ? (ke - 1) / BS - pg0 + 1 : 0;
+  for (int q = tid; q < min(npg, kAttnMaxPages); q += 512) pages[q] = bt[pg0 + q];
+  __syncthreads();
+
+  // this lane's copy: key 8 wave + lane / 8 of the tile, slot lane % 8, which
+  // holds global chunk (lane % 8) ^ (key & 7).  A wave's eight keys lie in
+  // one 16-token page (also after clamping to the split's last key), so the
+  // page and its base address are the same for the whole wave.
+  const int cgc = (lane & 7) ^ ((lane >> 3) & 7);
+  auto request = [&](int t, auto s_c) __attribute__((always_inline)) {
+    bf16_t* st = ring(s_c);
+    const int p0 = kb + min(t, ntiles - 1) * KT + wave * 8;  // the wave's first key
+    const int page = __builtin_amdgcn_readfirstlane(pages[min(p0, ke - 1) / BS - pg0]);
+    const int64_t base = (static_cast<int64_t>(page) * a.n_kv + g) * BS * D;
+    // clamped to the split's last key: finite values whose probability is zero
+    const int p = min(p0 + (lane >> 3), ke - 1);
+    const int off = (p % BS) * D + cgc * 8;
+    dma16(kc + base + off, st + wave * 8 * D);
+    dma16(vc + base + off, st + SK + wave * 8 * D);
+  };
+  constexpr int kWait = waitcnt_vm_lgkm0((ST - 2) * 2);
+
+  for (int qb = 0; qb < nqry; qb += 128) {
+    const int qn = qb + wave * 16 + (lane & 15);
+    const int row = r0 + qn / grp;
+    const int h = g * grp + qn % grp;
+    const bool active = qn < nqry && !a.rejected[row];
+    const int qpos = active ? a.pos[row] : -1;
+    int wave_qmin = active ? qpos : 0x7fffffff;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) wave_qmin = min(wave_qmin, __shfl_xor(wave_qmin, off, 64));
+    const bool wave_live = __builtin_amdgcn_readfirstlane(wave_qmin) != 0x7fffffff;
+    u32x4 qf[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qf[kk] = active ? load16(qin + (static_cast<int64_t>(row) * a.n_q + h) * D + 32 * kk + 8 * j) : zero;
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 o[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int t, auto s_c) __attribute__((always_inline)) {
+      const bf16_t* ks = ring(s_c);
+      const bf16_t* vs = ks + SK;
+      const int kt0 = kb + t * KT;
+      f32x4 st[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const int r = mt * 16 + (lane & 15);
+          const u32x4 af = *reinterpret_cast<const u32x4*>(&ks[r * D + (((4 * kk + j) ^ (r & 7)) << 3)]);
+          st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af),
+                                                           __builtin_bit_cast(bf16x8, qf[kk]), st[mt], 0, 0, 0);
+        }
+      const bool full = kt0 + KT <= ke && kt0 + KT - 1 <= wave_qmin;
+      float sv[16];
+      float mx = -INFINITY;
+      if (full) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            sv[mt * 4 + q] = st[mt][q];
+            mx = fmaxf(mx, st[mt][q]);
+          }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int p = kt0 + mt * 16 + 4 * j + q;
+            const float sc = (p < ke && p <= qpos) ? st[mt][q] : -INFINITY;
+            sv[mt * 4 + q] = sc;
+            mx = fmaxf(mx, sc);
+          }
+      }
+      mx = xor32_max(xor16_max(mx));
+      const float m_new = fmaxf(m_run, mx * sl2);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      // the running sums need rescaling only where the maximum rose (elsewhere
+      // the factor is exactly 1): skipped when it rose nowhere in the wave
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+        const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
+        l_run *= corr;
+#pragma unroll
+        for (int t2 = 0; t2 < DT; ++t2) o[t2] *= corr;
+      }
+      float rs = 0.f;
+      uint32_t pk[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[2 * e], sl2, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[2 * e + 1], sl2, -m_use));
+        rs += p0 + p1;
+        pk[e] = pack_bf16x2(p0, p1);
+      }
+      rs = xor32_sum(xor16_sum(rs));
+      l_run += rs;
+      m_run = m_new;
+      // transposing V reads: lane 4q + c of group j reads dims 16 t + 4 c ..
+      // + 3 of key 4 j + q (+ 16 for the second word, + 32 for the second
+      // half), i.e. chunk 2 t + c / 2, element 4 (c % 2) of that key row
+      const int kq = 4 * j + ((lane & 15) >> 2);
+      const int cq = lane & 3;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const u32x4 pb = {pk[4 * hf], pk[4 * hf + 1], pk[4 * hf + 2], pk[4 * hf + 3]};
+#pragma unroll
+        for (int t2 = 0; t2 < DT; ++t2) {
+          const int ra = kq + hf * 32, rb = ra + 16;
+          const int cc = 2 * t2 + (cq >> 1), e4 = 4 * (cq & 1);
+          const bf16_t* sa = vs + ra * D + ((cc ^ (ra & 7)) << 3) + e4;
+          const bf16_t* sb = vs + rb * D + ((cc ^ (rb & 7)) << 3) + e4;
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(sa));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(sb));
+          const u32x4 af = {__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                            __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y};
+          o[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af),
+                                                          __builtin_bit_cast(bf16x8, pb), o[t2], 0, 0, 0);
+        }
+      }
+    };
+    auto step = [&](int t, auto s_c) __attribute__((always_inline)) {
+      constexpr int S = decltype(s_c)::value;
+      __builtin_amdgcn_s_waitcnt(kWait);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      request(t + ST - 1, std::integral_constant<int, (S + ST - 1) % ST>{});
+      if (wave_live) compute(t, s_c);
+    };
+
+    if (ntiles > 0) {
+      static_for<ST - 1>([&](auto s_c) { request(decltype(s_c)::value, s_c); });
+      // the query fragments and the first stages: one wait, so no product in
+      // the loop waits on global memory the compiler tracks
+      __builtin_amdgcn_s_waitcnt(0);
+      int t = 0;
+      for (; t + ST <= ntiles; t += ST) static_for<ST>([&](auto s_c) { step(t + decltype(s_c)::value, s_c); });
+      static_for<ST - 1>([&](auto s_c) {
+        if (t + decltype(s_c)::value < ntiles) step(t + decltype(s_c)::value, s_c);
+      });
+      // every copy (clamped repeats included) has landed before the ring is
+      // reused or the workgroup ends
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    __syncthreads();
+    if (qn < nqry && !a.rejected[row]) {
+      float* out = a.partial + ((static_cast<int64_t>(row) * a.n_q + h) * a.splits + sp) * (D + 2);
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out[t * 16 + 4 * j + q] = o[t][q];
+      if (j == 0) {
+        out[D] = m_run == -INFINITY ? -INFINITY : m_run * 0.6931471805599453f;
+        out[D + 1] = l_run;
+      }
+    }
+  }
+}
+
 template <typename T, int D, int MAXS, int HPW>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   constexpr int DV = (D + 63) / 64;  // output dims per lane
@@ -437,7 +649,9 @@ void launch_mfma(const AttnArgs& a, dim3 grid, hipStream_t s) {
   // 64-dim heads: two workgroups per CU; 128-dim heads: one, with a deeper
   // register prefetch (two would spill)
   constexpr int DEPTH = D == 64 ? 2 : 3, OCC = D == 64 ? 4 : 2;
-  if (a.max_blocks <= (kAttnMaxPages - 8) * a.splits)
+  if (D == 64 && a.max_blocks <= (kAttnMaxPages - 8) * a.splits)
+    hipLaunchKernelGGL((attn_ring_kernel<4>), grid, dim3(512), 0, s, a);
+  else if (a.max_blocks <= (kAttnMaxPages - 8) * a.splits)
     hipLaunchKernelGGL((attn_mfma_kernel<D, DEPTH, OCC, true>), grid, dim3(512), 0, s, a);
   else
     hipLaunchKernelGGL((attn_mfma_kernel<D, DEPTH, OCC, false>), grid, dim3(512), 0, s, a);

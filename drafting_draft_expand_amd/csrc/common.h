@@ -120,6 +120,25 @@ __device__ __forceinline__ u32x4 load16_stream(const void* p) {
 }
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// 16 bytes per lane from global memory straight into LDS: lane l of the wave
+// writes lds + 16 l (lds wave-uniform).  Issued from inline assembly so that
+// the compiler's own wait-count bookkeeping, which cannot tell ring stages
+// apart and would wait for every copy before the next LDS read, leaves these
+// copies alone: the kernel waits for them itself.  M0 holds the LDS address
+// and needs one wait state before the copy reads it.
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const unsigned m = __builtin_amdgcn_readfirstlane(
+      static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds)));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(m) : "memory", "m0");
+#endif
+}
+
+// s_waitcnt immediate (gfx9 family): at most n vector-memory operations and no
+// LDS / scalar-memory operations outstanding (export count left at its maximum)
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4); }
+
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);

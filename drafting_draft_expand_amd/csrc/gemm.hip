@@ -423,24 +423,6 @@ __global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel
 // fragments are already in registers.  Requests past the split's last step
 // re-read that step (cache hits) so the steady state has no branches.
 
-// 16 bytes per lane from global memory straight into LDS: lane l of the wave
-// writes lds + 16 l (lds wave-uniform).  Issued from inline assembly so that
-// the compiler's own wait-count bookkeeping, which cannot tell ring stages
-// apart and would wait for every copy before the next LDS read, leaves these
-// copies alone: the kernel waits for them itself.  M0 holds the LDS address
-// and needs one wait state before the copy reads it.
-__device__ __forceinline__ void dma16(const void* g, void* lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  const unsigned m = __builtin_amdgcn_readfirstlane(
-      static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds)));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(m) : "memory", "m0");
-#endif
-}
-
-// s_waitcnt immediate (gfx9 family): at most n vector-memory operations and no
-// LDS / scalar-memory operations outstanding (export count left at its maximum)
-constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4); }
-
 // Row group of the tile-major W copy (packed_tile_bytes / launch_pack_tiles).
 constexpr int kTileGroup = 256;
 

@@ -1,10 +1,11 @@
-"""Static checks on the gfx950 code of the LDS-DMA ring GEMM (CPU only).
+"""Static checks on the gfx950 code of the LDS-DMA ring kernels (CPU only).
 
-The ring kernels issue their global -> LDS copies from inline assembly that
-writes M0 (the copy's LDS address).  M0 is a reserved register the compiler
-does not save around an asm statement, so the kernels are only correct while
-the compiler itself keeps nothing in M0: every M0 reference in their code must
-be one of those writes, each followed by its wait state and its copy.
+The ring GEMM and ring attention kernels issue their global -> LDS copies from
+inline assembly that writes M0 (the copy's LDS address).  M0 is a reserved
+register the compiler does not save around an asm statement, so the kernels are
+only correct while the compiler itself keeps nothing in M0: every M0 reference
+in their code must be one of those writes, each followed by its wait state and
+its copy.
 """
 
 import os
@@ -18,24 +19,25 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
-def _ring_bodies(tmp_path):
+def _ring_bodies(tmp_path, source, kernel):
     if not shutil.which(HIPCC) and not os.path.exists(HIPCC):
         pytest.skip("hipcc not available")
-    out = tmp_path / "gemm.s"
-    src = os.path.join(ROOT, "drafting_draft_expand_amd", "csrc", "gemm.hip")
+    out = tmp_path / (source + ".s")
+    src = os.path.join(ROOT, "drafting_draft_expand_amd", "csrc", source)
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
            "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S", "-o", str(out), src]
     subprocess.run(cmd, check=True, capture_output=True)
     text = out.read_text()
     bodies = {}
-    for m in re.finditer(r"^(_Z\S*gemm_ring_kernel\S*):.*?\n(.*?)s_endpgm", text, re.S | re.M):
+    for m in re.finditer(r"^(_Z\S*" + kernel + r"\S*):.*?\n(.*?)s_endpgm", text, re.S | re.M):
         bodies[m.group(1)] = [ln.strip() for ln in m.group(2).split("\n")
                               if ln.strip() and not ln.strip().startswith(";")]
     return bodies
 
 
-def test_ring_kernels_use_m0_only_for_their_copies(tmp_path):
-    bodies = _ring_bodies(tmp_path)
+@pytest.mark.parametrize("source,kernel", [("gemm.hip", "gemm_ring_kernel"), ("attention.hip", "attn_ring_kernel")])
+def test_ring_kernels_use_m0_only_for_their_copies(tmp_path, source, kernel):
+    bodies = _ring_bodies(tmp_path, source, kernel)
     assert bodies, "no ring kernel instantiated"
     for name, lines in bodies.items():
         writes = copies = 0
