@@ -505,7 +505,7 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
         g.w_a = L.wq; g.n_a = qd; g.w_b = L.wk; g.n_b = kvd; g.w_c = L.wv;
         g.pk_a = P ? P->qkv : nullptr;
         g.rope.n_q = d.n_q; g.rope.n_kv = d.n_kv; g.rope.d = d.head_dim; g.rope.block_size = d.block_size;
-        g.rope.freq = m->freq; g.rope.pos = draft_pos; g.rope.slot = slot_mapping;
+        g.rope.slot = slot_mapping;
         g.rope.rejected = is_rejected; g.rope.q_out = qrot; g.rope.k_cache = k_cache[l];
         g.rope.v_cache = v_cache[l]; g.rope.table = rope_tab;
         if ((st = proj(g, pe::Epi::QkvRope)) != PE_OK) return st;

@@ -66,14 +66,13 @@ enum class AMode {
 // cache at the row's slot (nothing for slot -1).
 struct RopeOut {
   int n_q, n_kv, d, block_size;
-  RopeFreq freq;
-  const int32_t* pos;
   const int64_t* slot;
   const uint8_t* rejected;
   void* q_out;                 // [M, n_q * d] model dtype
   void *k_cache, *v_cache;     // [blocks, n_kv, block_size, d]
-  // [M][d / 2] (cos, sin) of pos[m] * freq.inv[j] as rope_cos_sin gives them
-  // (written by the RMSNorm before the projection); required
+  // [M][d / 2] (cos, sin) of row m's rotary angle j (its position times the
+  // j-th inverse frequency, as rope_cos_sin evaluates them), written by the
+  // RMSNorm before the projection; required
   const float2* table;
 };
 
