@@ -50,12 +50,16 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline DType dt(const pe_model* m) { return m->d.dtype == PE_F32 ? DType::F32 : DType::BF16; }
 
-// KV-range splits per (sequence, kv head): about 2048 workgroups (eight per
-// CU over the launch) so that the per-tile softmax work of long contexts
-// spreads over the chip, without multiplying the partial-result traffic.
-int attention_splits(int c, int n_kv) {
+// KV-range splits per (sequence, kv head).  The bf16 LDS-ring kernels take
+// the longest ranges first, so about two workgroups per slot suffice to
+// balance the chip: 1024 for 64-dim heads (two workgroups per CU), 512 for
+// 128-dim heads (one); fewer splits also mean less partial-result traffic.
+// The other kernels take about 2048 workgroups (eight per CU) so that the
+// per-tile softmax work of long contexts spreads over the chip.
+int attention_splits(int c, int n_kv, int head_dim, pe_dtype dtype) {
   const int base = c * n_kv;
-  int s = (2048 + base - 1) / base;
+  const int target = dtype != PE_BF16 ? 2048 : head_dim == 64 ? 1024 : head_dim == 128 ? 512 : 2048;
+  int s = (target + base - 1) / base;
   if (s < 1) s = 1;
   if (s > pe::kAttnMaxSplits) s = pe::kAttnMaxSplits;
   return s;
@@ -80,7 +84,7 @@ Workspace plan_workspace(const pe_model* m, int c, int K, int N) {
   if (qd > act_cols) act_cols = qd;
   if (d.inter > act_cols) act_cols = d.inter;
   Workspace w{};
-  w.splits = attention_splits(c, d.n_kv);
+  w.splits = attention_splits(c, d.n_kv, d.head_dim, d.dtype);
   w.lm_parts = 4096;  // upper bound on LM-head workgroups (grid is capped at 2 per CU)
   size_t off = 0;
   w.x = off;         off += align_up(size_t(N) * H * 4);

@@ -384,23 +384,27 @@ __global__ __launch_bounds__(512, OCC) void attn_mfma_kernel(AttnArgs a) {
 // first use: lane s reads the statistics of split s, and every lane reads its
 // output dims (lane, lane + 64) of all splits, splits past S clamped to the
 // last one and weighted 0, so the kernel waits for memory once.
-// bf16, 64-dim heads, a split's page numbers in LDS: the same products with
-// K and V copied straight into a ring of ST LDS stages (global_load_lds, no
-// register staging), so the copies of later tiles run while the waves compute
-// instead of between their products.  A stage holds the tile's 64 K rows then
-// its 64 V rows, 128 bytes each, unpadded, 16-byte chunk c of key row r at
+// bf16, 64- or 128-dim heads, a split's page numbers in LDS: the same
+// products with K and V copied straight into a ring of ST LDS stages
+// (global_load_lds, no register staging), so the copies of later tiles run
+// while the waves compute instead of between their products.  A stage holds
+// the tile's 64 K rows then its 64 V rows, each as D / 64 planes of 64 dims
+// (128 bytes a row, unpadded), 16-byte chunk c of key row r of a plane at
 // slot c ^ (r & 7): the score-fragment reads (16 rows x 4 chunks) and the
-// transposing V reads both spread over the banks.  Wave w copies keys
-// 8w..8w+7 of K and of V (one KiB each; eight keys never straddle a 16-token
-// page).  Step t waits until its own copies of stage t have landed (ST-2
-// stages still in flight), meets the other waves, requests tile t+ST-1 into
-// the slot step t-1 used, then computes.
-template <int ST>
-__global__ __launch_bounds__(512, 4) void attn_ring_kernel(AttnArgs a) {
-  constexpr int D = 64, KT = 64;
+// transposing V reads both spread over the banks, and a 128-dim tile is read
+// as two 64-dim ones.  Wave w copies keys 8w..8w+7 of each plane of K and of
+// V (one KiB each; eight keys never straddle a 16-token page).  Step t waits
+// until its own copies of stage t have landed (ST-2 stages still in flight),
+// meets the other waves, requests tile t+ST-1 into the slot step t-1 used,
+// then computes.  64-dim heads fit two workgroups per CU, 128-dim heads one.
+template <int D, int ST>
+__global__ __launch_bounds__(512, D == 64 ? 4 : 2) void attn_ring_kernel(AttnArgs a) {
+  constexpr int KT = 64, PL = D / 64;  // keys per tile, 64-dim planes
   constexpr int DT = D / 16, KK = D / 32;
   constexpr int SK = KT * D;  // elements of one K (or V) tile
-  constexpr int BS = 16;      // KV page size (the only one the library accepts)
+  constexpr int SP = KT * 64;  // elements of one plane of a tile
+  constexpr int BS = 16;       // KV page size (the only one the library accepts)
+  static_assert(D == 64 || D == 128, "64- or 128-dim heads");
   static_assert(ST >= 3 && ST <= 4, "three or four ring stages");
   typedef short v4i16 __attribute__((ext_vector_type(4)));
   __shared__ __attribute__((aligned(16))) bf16_t R0[2 * SK];
@@ -417,7 +421,27 @@ __global__ __launch_bounds__(512, 4) void attn_ring_kernel(AttnArgs a) {
   };
   const int tid = threadIdx.x, lane = tid & 63, j = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int sp = blockIdx.x, g = blockIdx.y, i = blockIdx.z;
+  const int sp = blockIdx.x, g = blockIdx.y;
+  // Longest KV ranges first: the workgroups of launch slot z take the
+  // sequence of rank z by decreasing KV length (ties by index), so the
+  // longest splits start at once and the short ones fill in behind them
+  // instead of a long one starting last (one sequence, or more than 512:
+  // launch order).
+  __shared__ int seq_sel;
+  int i = blockIdx.z;
+  if (a.c > 1 && a.c <= 512) {
+    if (tid < a.c) {
+      const int mine = a.kv_lens[tid];
+      int rank = 0;
+      for (int o = 0; o < a.c; ++o) {
+        const int other = a.kv_lens[o];
+        rank += other > mine || (other == mine && o < tid);
+      }
+      if (rank == static_cast<int>(blockIdx.z)) seq_sel = tid;
+    }
+    __syncthreads();
+    i = __builtin_amdgcn_readfirstlane(seq_sel);
+  }
   const int grp = a.n_q / a.n_kv;
   const int r0 = a.cu_draft[i], r1 = a.cu_draft[i + 1];
   const int kvlen = a.kv_lens[i];
@@ -450,10 +474,13 @@ __global__ __launch_bounds__(512, 4) void attn_ring_kernel(AttnArgs a) {
     // clamped to the split's last key: finite values whose probability is zero
     const int p = min(p0 + (lane >> 3), ke - 1);
     const int off = (p % BS) * D + cgc * 8;
-    dma16(kc + base + off, st + wave * 8 * D);
-    dma16(vc + base + off, st + SK + wave * 8 * D);
+#pragma unroll
+    for (int pl = 0; pl < PL; ++pl) {
+      dma16(kc + base + off + pl * 64, st + pl * SP + wave * 8 * 64);
+      dma16(vc + base + off + pl * 64, st + SK + pl * SP + wave * 8 * 64);
+    }
   };
-  constexpr int kWait = waitcnt_vm_lgkm0((ST - 2) * 2);
+  constexpr int kWait = waitcnt_vm_lgkm0((ST - 2) * 2 * PL);
 
   for (int qb = 0; qb < nqry; qb += 128) {
     const int qn = qb + wave * 16 + (lane & 15);
@@ -486,7 +513,8 @@ __global__ __launch_bounds__(512, 4) void attn_ring_kernel(AttnArgs a) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const int r = mt * 16 + (lane & 15);
-          const u32x4 af = *reinterpret_cast<const u32x4*>(&ks[r * D + (((4 * kk + j) ^ (r & 7)) << 3)]);
+          const bf16_t* kp = ks + (kk >> 1) * SP + r * 64;  // plane kk / 2, its chunk 4 (kk % 2) + j
+          const u32x4 af = *reinterpret_cast<const u32x4*>(&kp[((4 * (kk & 1) + j) ^ (r & 7)) << 3]);
           st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af),
                                                            __builtin_bit_cast(bf16x8, qf[kk]), st[mt], 0, 0, 0);
         }
@@ -537,7 +565,8 @@ __global__ __launch_bounds__(512, 4) void attn_ring_kernel(AttnArgs a) {
       m_run = m_new;
       // transposing V reads: lane 4q + c of group j reads dims 16 t + 4 c ..
       // + 3 of key 4 j + q (+ 16 for the second word, + 32 for the second
-      // half), i.e. chunk 2 t + c / 2, element 4 (c % 2) of that key row
+      // half), i.e. chunk 2 (t % 4) + c / 2, element 4 (c % 2) of that key
+      // row in plane t / 4
       const int kq = 4 * j + ((lane & 15) >> 2);
       const int cq = lane & 3;
 #pragma unroll
@@ -546,9 +575,10 @@ __global__ __launch_bounds__(512, 4) void attn_ring_kernel(AttnArgs a) {
 #pragma unroll
         for (int t2 = 0; t2 < DT; ++t2) {
           const int ra = kq + hf * 32, rb = ra + 16;
-          const int cc = 2 * t2 + (cq >> 1), e4 = 4 * (cq & 1);
-          const bf16_t* sa = vs + ra * D + ((cc ^ (ra & 7)) << 3) + e4;
-          const bf16_t* sb = vs + rb * D + ((cc ^ (rb & 7)) << 3) + e4;
+          const int cc = 2 * (t2 & 3) + (cq >> 1), e4 = 4 * (cq & 1);
+          const bf16_t* vp = vs + (t2 >> 2) * SP;
+          const bf16_t* sa = vp + ra * 64 + ((cc ^ (ra & 7)) << 3) + e4;
+          const bf16_t* sb = vp + rb * 64 + ((cc ^ (rb & 7)) << 3) + e4;
           const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(sa));
           const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(sb));
           const u32x4 af = {__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
@@ -649,10 +679,8 @@ void launch_mfma(const AttnArgs& a, dim3 grid, hipStream_t s) {
   // 64-dim heads: two workgroups per CU; 128-dim heads: one, with a deeper
   // register prefetch (two would spill)
   constexpr int DEPTH = D == 64 ? 2 : 3, OCC = D == 64 ? 4 : 2;
-  if (D == 64 && a.max_blocks <= (kAttnMaxPages - 8) * a.splits)
-    hipLaunchKernelGGL((attn_ring_kernel<4>), grid, dim3(512), 0, s, a);
-  else if (a.max_blocks <= (kAttnMaxPages - 8) * a.splits)
-    hipLaunchKernelGGL((attn_mfma_kernel<D, DEPTH, OCC, true>), grid, dim3(512), 0, s, a);
+  if (a.max_blocks <= (kAttnMaxPages - 8) * a.splits)
+    hipLaunchKernelGGL((attn_ring_kernel<D, 3>), grid, dim3(512), 0, s, a);
   else
     hipLaunchKernelGGL((attn_mfma_kernel<D, DEPTH, OCC, false>), grid, dim3(512), 0, s, a);
 }

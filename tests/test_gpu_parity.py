@@ -207,6 +207,25 @@ def test_forward_bf16_many_rows_ragged():
     _forward_case(wl)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_forward_bf16_equal_kv_lengths(d):
+    """Every sequence with the same KV length (equal contexts, nothing accepted):
+    the attention kernels order sequences longest first and fall back to the
+    sequence index on ties; each sequence must still be attended exactly once."""
+    spec = synth.ModelSpec(hidden=256, vocab=600, n_layers=1, n_q=4, n_kv=2, head_dim=d, inter=384)
+    wl = synth.Workload(f"equal-kv-d{d}", spec, c=9, K=3, ctx_lo=200, ctx_hi=200, accept_hi=0, seed=90 + d)
+    _forward_case(wl)
+
+
+def test_forward_bf16_d128_mixed_contexts():
+    """bf16 128-dim heads over contexts from empty to several hundred tokens:
+    KV splits with no tile, a partial last tile, sequences in longest-first
+    order."""
+    spec = synth.ModelSpec(hidden=256, vocab=600, n_layers=1, n_q=4, n_kv=2, head_dim=128, inter=384)
+    wl = synth.Workload("mixed-kv-d128", spec, c=11, K=4, ctx_lo=0, ctx_hi=900, accept_hi=4, seed=93)
+    _forward_case(wl)
+
+
 def test_forward_gptoss_c1_full():
     _forward_case(synth.WORKLOADS["gptoss20b-bf16-c1-k7"])
 
