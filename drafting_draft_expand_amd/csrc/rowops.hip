@@ -21,6 +21,18 @@ __global__ __launch_bounds__(256) void fc_input_kernel(int H_bytes, const int32_
   }
 }
 
+// four consecutive elements as fp32 (p 8-byte aligned for bf16, 16 for fp32)
+template <typename T>
+__device__ __forceinline__ f32x4 load4_f32(const T* p) {
+  if constexpr (sizeof(T) == 4) {
+    return *reinterpret_cast<const f32x4*>(p);
+  } else {
+    const uint2 r = *reinterpret_cast<const uint2*>(p);
+    return f32x4{bf16_to_f32(static_cast<bf16_t>(r.x & 0xffffu)), bf16_to_f32(static_cast<bf16_t>(r.x >> 16)),
+                 bf16_to_f32(static_cast<bf16_t>(r.y & 0xffffu)), bf16_to_f32(static_cast<bf16_t>(r.y >> 16))};
+  }
+}
+
 // out[i] = x[row] / sqrt(mean(x[row]^2) + eps) * gain, rounded to the operand
 // dtype; one workgroup per row, row = row_idx ? row_idx[i] : i.  With NS > 0
 // the row is first completed from the split partials of the projection that
@@ -71,6 +83,11 @@ __global__ __launch_bounds__(1024) void rmsnorm_kernel(int H, const int32_t* __r
       ss += q[0] * q[0] + q[1] * q[1] + q[2] * q[2] + q[3] * q[3];
     }
   }
+  // the gains are loaded before the reduction so that their latency overlaps it
+  f32x4 gv[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    gv[u] = load4_f32(gain + 4 * min(static_cast<int>(threadIdx.x + blockDim.x * u), nv - 1));
   ss = wave_sum(ss);
   const int nw = blockDim.x >> 6;
   if ((threadIdx.x & 63) == 0) wave_ss[threadIdx.x >> 6] = ss;
@@ -91,7 +108,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_kernel(int H, const int32_t* __r
     const int k = 4 * v;
     T* o = out + row_base + (out_group > 0 ? static_cast<int64_t>(k / 32) * out_group * 32 + k % 32 : k);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = Elem<T>::from_f32(q[e] * scale * Elem<T>::to_f32(gain[k + e]));
+    for (int e = 0; e < 4; ++e) o[e] = Elem<T>::from_f32(q[e] * scale * gv[u][e]);
   }
 }
 
