@@ -379,11 +379,6 @@ __global__ __launch_bounds__(512, OCC) void attn_mfma_kernel(AttnArgs a) {
   }
 }
 
-// out[row, h, :] = sum_s acc_s * e^{m_s - M} / sum_s l_s * e^{m_s - M};
-// one 64-thread workgroup per (row, head).  Every load is issued before the
-// first use: lane s reads the statistics of split s, and every lane reads its
-// output dims (lane, lane + 64) of all splits, splits past S clamped to the
-// last one and weighted 0, so the kernel waits for memory once.
 // bf16, 64- or 128-dim heads, a split's page numbers in LDS: the same
 // products with K and V copied straight into a ring of ST LDS stages
 // (global_load_lds, no register staging), so the copies of later tiles run
@@ -456,6 +451,28 @@ __global__ __launch_bounds__(512, D == 64 ? 4 : 2) void attn_ring_kernel(AttnArg
   const bf16_t* vc = static_cast<const bf16_t*>(a.v_cache);
   const int32_t* bt = a.block_table + static_cast<int64_t>(i) * a.max_blocks;
   const u32x4 zero = {0u, 0u, 0u, 0u};
+  // This lane's query of block qb: its row (clamped into the sequence for the
+  // loads), head, rejected flag, position and fragments, all loaded without a
+  // branch so that they are in flight together; those of the first block go
+  // out before the page list is fetched.
+  struct Query {
+    int qn, row, h;
+    bool rej;
+    int pos;
+    u32x4 qf[KK];
+  };
+  auto load_query = [&](int qb) __attribute__((always_inline)) {
+    Query q;
+    q.qn = qb + wave * 16 + (lane & 15);
+    q.row = min(r0 + q.qn / grp, r1 - 1);
+    q.h = g * grp + q.qn % grp;
+    q.rej = a.rejected[q.row] != 0;
+    q.pos = a.pos[q.row];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) q.qf[kk] = load16(qin + (static_cast<int64_t>(q.row) * a.n_q + q.h) * D + 32 * kk + 8 * j);
+    return q;
+  };
+  Query qnext = load_query(0);
   const int pg0 = kb / BS;
   const int npg = ke > kb ? (ke - 1) / BS - pg0 + 1 : 0;
   for (int q = tid; q < min(npg, kAttnMaxPages); q += 512) pages[q] = bt[pg0 + q];
@@ -483,19 +500,17 @@ __global__ __launch_bounds__(512, D == 64 ? 4 : 2) void attn_ring_kernel(AttnArg
   constexpr int kWait = waitcnt_vm_lgkm0((ST - 2) * 2 * PL);
 
   for (int qb = 0; qb < nqry; qb += 128) {
-    const int qn = qb + wave * 16 + (lane & 15);
-    const int row = r0 + qn / grp;
-    const int h = g * grp + qn % grp;
-    const bool active = qn < nqry && !a.rejected[row];
-    const int qpos = active ? a.pos[row] : -1;
+    const Query cur = qnext;
+    const int qn = cur.qn, row = cur.row, h = cur.h;
+    const bool active = qn < nqry && !cur.rej;
+    const int qpos = active ? cur.pos : -1;
     int wave_qmin = active ? qpos : 0x7fffffff;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) wave_qmin = min(wave_qmin, __shfl_xor(wave_qmin, off, 64));
     const bool wave_live = __builtin_amdgcn_readfirstlane(wave_qmin) != 0x7fffffff;
     u32x4 qf[KK];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      qf[kk] = active ? load16(qin + (static_cast<int64_t>(row) * a.n_q + h) * D + 32 * kk + 8 * j) : zero;
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = active ? cur.qf[kk] : zero;
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 o[DT];
 #pragma unroll
@@ -612,7 +627,7 @@ __global__ __launch_bounds__(512, D == 64 ? 4 : 2) void attn_ring_kernel(AttnArg
       __builtin_amdgcn_s_waitcnt(0);
     }
     __syncthreads();
-    if (qn < nqry && !a.rejected[row]) {
+    if (active) {
       float* out = a.partial + ((static_cast<int64_t>(row) * a.n_q + h) * a.splits + sp) * (D + 2);
 #pragma unroll
       for (int t = 0; t < DT; ++t)
@@ -623,9 +638,16 @@ __global__ __launch_bounds__(512, D == 64 ? 4 : 2) void attn_ring_kernel(AttnArg
         out[D + 1] = l_run;
       }
     }
+    if (qb + 128 < nqry) qnext = load_query(qb + 128);
   }
 }
 
+// out[row, h, :] = sum_s acc_s * e^{m_s - M} / sum_s l_s * e^{m_s - M} (zero
+// for a rejected row); four waves per workgroup, HPW heads per wave.  Every
+// load is issued before the first use: lane s reads the statistics of split
+// s, and every lane reads its output dims (lane, lane + 64) of all splits,
+// splits past S clamped to the last one and weighted 0, so the kernel waits
+// for memory once.
 template <typename T, int D, int MAXS, int HPW>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   constexpr int DV = (D + 63) / 64;  // output dims per lane
@@ -639,10 +661,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     const int h = h0 + hh;
     if (h >= a.n_q) break;
     T* out = static_cast<T*>(a.out) + (static_cast<int64_t>(row) * a.n_q + h) * D;
-    if (rejected) {
-      for (int dd = lane; dd < D; dd += 64) out[dd] = Elem<T>::from_f32(0.f);
-      continue;
-    }
+    // (a rejected row's partials were never written: they are read with the
+    // rest, so no load waits for the flag, and discarded)
     const float* p = a.partial + (static_cast<int64_t>(row) * a.n_q + h) * S * (D + 2);
     const int sl = min(lane, S - 1);
     const float m_l = p[sl * (D + 2) + D];
@@ -670,7 +690,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     const float inv = 1.f / den;
 #pragma unroll
     for (int e = 0; e < DV; ++e)
-      if (lane + 64 * e < D) out[lane + 64 * e] = Elem<T>::from_f32(num[e] * inv);
+      if (lane + 64 * e < D) out[lane + 64 * e] = Elem<T>::from_f32(rejected ? 0.f : num[e] * inv);
   }
 }
 
