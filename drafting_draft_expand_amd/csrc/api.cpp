@@ -415,9 +415,10 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
   const int H = d.hidden, qd = d.n_q * d.head_dim, kvd = d.n_kv * d.head_dim, S = c * K;
   {
     // every projection's activation slice must fit the kernel's LDS budget
-    const int shapes[][2] = {{N, 2 * H}, {N, H}, {N, qd}, {N, d.inter}, {S, H}};
+    const int shapes[][2] = {{N, 2 * H}, {N, H}, {N, qd}, {N, d.inter}};
     for (const auto& sh : shapes)
       if (pe::gemv_lds_bytes(sh[0], sh[1], t) > 160 * 1024) return PE_EUNSUPPORTED;
+    if (pe::gemv_lds_bytes(S, H, t, pe::Epi::Argmax) > 160 * 1024) return PE_EUNSUPPORTED;
   }
   char* wb = static_cast<char*>(workspace);
   float* x = reinterpret_cast<float*>(wb + ws.x);

@@ -4,7 +4,7 @@
 // both kernels are organised around reading W exactly once from HBM with
 // 16-byte loads and enough of them in flight per CU:
 //
-// gemv_lds_kernel (M <= 8 per slice, and every fp32 model):
+// gemv_lds_kernel (every fp32 model, and the bf16 LM head over M <= 8 rows):
 //   the activation slice is staged once per workgroup in LDS; each wave owns R
 //   consecutive output rows, every lane streams 16-byte pieces of those rows
 //   (two k-steps in flight, non-temporal) and multiplies them with the matching
@@ -12,9 +12,11 @@
 //   per-lane partial sums are folded across the wave with a reduce-scatter, so
 //   every lane ends with one finished dot product and applies the epilogue.
 //
-// mfma_skinny_kernel (bf16, 8 < M <= 16):
+// mfma_skinny_kernel (bf16, M <= 16; the LM head from 9 rows):
 //   at 14-16 rows the VALU would be near saturation at full HBM rate, so the
-//   products run on v_mfma_f32_16x16x32_bf16: the activation rows are the A
+//   products run on v_mfma_f32_16x16x32_bf16 (fewer rows only pad the
+//   fragment, and the packed weights stream better than the LDS kernel's
+//   row-major ones for the layer projections): the activation rows are the A
 //   operand (one 16-byte piece per lane per k-step) and 16 weight rows are the
 //   B operand.  The weights come from a packed copy in MFMA fragment order
 //   (each wave load one contiguous KiB) or, for the LM head and unpacked
@@ -527,10 +529,21 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs p) {
 
 // ------------------------------------------------------------------ dispatch
 // Smallest activation-row tile that covers M (one pass over the weights),
-// 16-row slices beyond that.
-int gemv_m_tile(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
+// 16-row slices beyond that.  The bf16 LM head over 3..8 rows takes the 8-row
+// tile, whose launch shape streams the vocabulary fastest (its padding rows
+// cost VALU time only): 182 against 201 us over 3 rows at V = 201088.
+int gemv_m_tile(int M, Epi epi, DType dt) {
+  if (epi == Epi::Argmax && dt == DType::BF16 && M >= 3 && M <= 8) return 8;
+  return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
+}
 
-bool use_mfma(int M, int K, DType dt) { return dt == DType::BF16 && M > 8 && M <= 16 && K % 32 == 0; }
+// bf16 projections of up to 16 rows stream their weights through the MFMA
+// kernel (padding rows of the 16-row fragment cost nothing at the HBM rate);
+// the LM head over at most 8 rows keeps the LDS kernel, which streams its
+// row-major weights fastest.
+bool use_mfma(int M, int K, DType dt, Epi epi) {
+  return dt == DType::BF16 && M >= 1 && M <= 16 && K % 32 == 0 && (epi != Epi::Argmax || M > 8);
+}
 
 // Launch shape of the weight-streaming MFMA kernel.
 //   * Row-major weights, or epilogues that need whole sums in one workgroup
@@ -637,7 +650,7 @@ hipError_t launch_lds(GemvArgs& a, dim3 grid, hipStream_t s) {
 
 template <typename TW, Epi EPI, AMode MODE>
 hipError_t launch_valu(GemvArgs& a, int num_cus, hipStream_t s) {
-  const int m_tile = gemv_m_tile(a.M);
+  const int m_tile = gemv_m_tile(a.M, EPI, sizeof(TW) == 2 ? DType::BF16 : DType::F32);
   const int R = m_tile >= 16 ? 4 : m_tile >= 8 ? 8 : 16;  // R * MT <= 64
   const int rg = EPI == Epi::SiluMul ? R / 2 : R;
   const int groups = (a.Nout + rg - 1) / rg;
@@ -660,22 +673,22 @@ hipError_t launch_valu(GemvArgs& a, int num_cus, hipStream_t s) {
 
 }  // namespace
 
-ProjKernel proj_kernel(int M, int K, DType dt) {
+ProjKernel proj_kernel(int M, int K, DType dt, Epi epi) {
   if (dt == DType::BF16 && M > 16 && K % 64 == 0) return ProjKernel::Tiled;
-  if (use_mfma(M, K, dt)) return ProjKernel::Skinny;
+  if (use_mfma(M, K, dt, epi)) return ProjKernel::Skinny;
   return ProjKernel::Lds;
 }
 
 bool gemv_uses_mfma(int M, int K, DType dt) { return proj_kernel(M, K, dt) != ProjKernel::Lds; }
 
 int gemv_grid_x(int M, int Nout, Epi epi, DType dt, int num_cus, int K) {
-  if (proj_kernel(M, K, dt) == ProjKernel::Tiled) return gemm_parts(M, Nout, num_cus);
-  if (use_mfma(M, K, dt)) {
+  if (proj_kernel(M, K, dt, epi) == ProjKernel::Tiled) return gemm_parts(M, Nout, num_cus);
+  if (use_mfma(M, K, dt, epi)) {
     // the argmax epilogue always runs one tile per group on row-major weights
     const int T = (Nout + 15) / 16;
     return T < num_cus * 4 ? T : num_cus * 4;
   }
-  const int m_tile = gemv_m_tile(M);
+  const int m_tile = gemv_m_tile(M, epi, dt);
   const int R = m_tile >= 16 ? 4 : m_tile >= 8 ? 8 : 16;
   const int rg = epi == Epi::SiluMul ? R / 2 : R;
   int gx = ((Nout + rg - 1) / rg + 3) / 4;
@@ -683,9 +696,9 @@ int gemv_grid_x(int M, int Nout, Epi epi, DType dt, int num_cus, int K) {
   return gx < 1 ? 1 : gx;
 }
 
-size_t gemv_lds_bytes(int M, int K, DType dt) {
-  if (proj_kernel(M, K, dt) != ProjKernel::Lds) return 0;
-  return static_cast<size_t>(gemv_m_tile(M)) * K * elem_bytes(dt);
+size_t gemv_lds_bytes(int M, int K, DType dt, Epi epi) {
+  if (proj_kernel(M, K, dt, epi) != ProjKernel::Lds) return 0;
+  return static_cast<size_t>(gemv_m_tile(M, epi, dt)) * K * elem_bytes(dt);
 }
 
 // Supported (epilogue, operand) pairs: every epilogue with a plain operand on
@@ -695,8 +708,8 @@ size_t gemv_lds_bytes(int M, int K, DType dt) {
 hipError_t launch_gemv(GemvArgs& a, Epi epi, DType dt, int num_cus, hipStream_t s) {
   a.splits = 1;
   if (epi == Epi::QkvRope && !a.rope.table) return hipErrorInvalidValue;
-  if (proj_kernel(a.M, a.K, dt) == ProjKernel::Tiled) return launch_gemm(a, epi, num_cus, s);
-  if (use_mfma(a.M, a.K, dt)) {
+  if (proj_kernel(a.M, a.K, dt, epi) == ProjKernel::Tiled) return launch_gemm(a, epi, num_cus, s);
+  if (use_mfma(a.M, a.K, dt, epi)) {
     if (a.amode == AMode::Plain) {
       switch (epi) {
         case Epi::Store: return launch_mfma<Epi::Store, AMode::Plain>(a, num_cus, s);

@@ -132,15 +132,16 @@ struct GemvArgs {
   int splits;                  // filled by the launcher: K splits left in part (1: y written)
 };
 constexpr int kMaxSplits = 8;
-// Kernel families: LDS-staged dot2 GEMV (M <= 8 per slice, fp32), weight-streaming
-// MFMA (bf16, 8 < M <= 16), tiled MFMA GEMM (bf16, M > 16, K % 64 == 0).
+// Kernel families: LDS-staged dot2 GEMV (fp32, and the bf16 LM head over at most
+// 8 rows), weight-streaming MFMA (bf16, M <= 16), tiled MFMA GEMM (bf16, M > 16,
+// K % 64 == 0).  The epilogue is that of the projection (argmax: the LM head).
 enum class ProjKernel { Lds = 0, Skinny = 1, Tiled = 2 };
-ProjKernel proj_kernel(int M, int K, DType dt);
+ProjKernel proj_kernel(int M, int K, DType dt, Epi epi = Epi::Store);
 hipError_t launch_gemm(GemvArgs& a, Epi epi, int num_cus, hipStream_t s);
 int gemm_parts(int M, int Nout, int num_cus);  // argmax candidates per row of the tiled kernel
 hipError_t launch_gemv(GemvArgs& a, Epi epi, DType dt, int num_cus, hipStream_t s);
 int gemv_grid_x(int M, int Nout, Epi epi, DType dt, int num_cus, int K);
-size_t gemv_lds_bytes(int M, int K, DType dt);  // dynamic LDS of the chosen kernel
+size_t gemv_lds_bytes(int M, int K, DType dt, Epi epi = Epi::Store);  // dynamic LDS of the chosen kernel
 bool gemv_uses_mfma(int M, int K, DType dt);
 
 // Packed copy of W for the weight-streaming MFMA kernel: ceil(Nout / 16) tiles

@@ -144,11 +144,23 @@ def test_forward_head_dims(dtype, d):
 
 
 def test_forward_bf16_few_rows_unfused():
-    """c=1, K=3: 6 draft rows, so every projection takes the VALU path with the
-    separate gather / norm / RoPE kernels."""
-    spec = synth.ModelSpec(hidden=256, vocab=1000, n_layers=1, n_q=8, n_kv=2, head_dim=64, inter=512)
+    """c=1, K=3: 6 draft rows with a hidden size that is not a multiple of 32
+    (200), so every projection takes the VALU path with the separate gather /
+    norm / RoPE kernels."""
+    spec = synth.ModelSpec(hidden=200, vocab=1000, n_layers=1, n_q=8, n_kv=2, head_dim=64, inter=512)
     wl = synth.Workload("few-rows-bf16", spec, c=1, K=3, ctx_lo=30, ctx_hi=90, accept_hi=3, seed=43)
     _forward_case(wl)
+
+
+@pytest.mark.parametrize("pack", [True, False])
+@pytest.mark.parametrize("K", [1, 3])
+def test_forward_bf16_fewest_rows_mfma(K, pack):
+    """One sequence, 2 and 6 draft rows: the weight-streaming MFMA projections
+    with most of the 16-row fragment padding, while the LM head over 1 and 3
+    sampled rows stays on the LDS kernel."""
+    spec = synth.ModelSpec(hidden=544, vocab=1000, n_layers=1, n_q=6, n_kv=2, head_dim=32, inter=5120)
+    wl = synth.Workload(f"fewest-rows-mfma-k{K}", spec, c=1, K=K, ctx_lo=40, ctx_hi=200, accept_hi=K, seed=70 + K)
+    _forward_case(wl, pack=pack)
 
 
 @pytest.mark.parametrize("pack", [True, False])
