@@ -209,6 +209,16 @@ def test_forward_bf16_many_sampled_rows(pack):
     _forward_case(wl, pack=pack)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_forward_bf16_mid_rows(d):
+    """200 draft rows (two 128-row tiles, the second ragged): the register-staged
+    tiled GEMM with narrow tiles, 128 x 64 for q/k/v with RoPE and gate/up, and
+    K split into partials for the residual projections."""
+    spec = synth.ModelSpec(hidden=256, vocab=900, n_layers=1, n_q=4, n_kv=2, head_dim=d, inter=320)
+    wl = synth.Workload(f"mid-rows-d{d}", spec, c=20, K=5, ctx_lo=10, ctx_hi=200, accept_hi=5, seed=95 + d)
+    _forward_case(wl)
+
+
 def test_forward_bf16_many_rows_ragged():
     """About 300 draft rows on a drafter whose widths are not multiples of the
     ring kernel's tiles: hidden 320 (two 256-column tiles, the second ragged),
