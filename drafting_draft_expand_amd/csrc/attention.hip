@@ -696,8 +696,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 
 template <int D>
 void launch_mfma(const AttnArgs& a, dim3 grid, hipStream_t s) {
-  // 64-dim heads: two workgroups per CU; 128-dim heads: one, with a deeper
-  // register prefetch (two would spill)
+  // The LDS-DMA ring whenever a split's page numbers fit in LDS, else the
+  // register-staged kernel reading the block table (64-dim heads: two
+  // workgroups per CU; 128-dim heads: one, with a deeper register prefetch,
+  // as two would spill)
   constexpr int DEPTH = D == 64 ? 2 : 3, OCC = D == 64 ? 4 : 2;
   if (a.max_blocks <= (kAttnMaxPages - 8) * a.splits)
     hipLaunchKernelGGL((attn_ring_kernel<D, 3>), grid, dim3(512), 0, s, a);
