@@ -248,6 +248,20 @@ def test_forward_bf16_d128_mixed_contexts():
     _forward_case(wl)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_forward_bf16_page_list_beyond_lds(d):
+    """A block table wider than a KV split's page list can hold in LDS (17 300
+    columns, those past each sequence's pages unused): attention takes the
+    register-staged kernel that reads the block table directly."""
+    spec = synth.ModelSpec(hidden=256, vocab=600, n_layers=1, n_q=4, n_kv=2, head_dim=d, inter=384)
+    wl = synth.Workload(f"wide-table-d{d}", spec, c=3, K=3, ctx_lo=50, ctx_hi=400, accept_hi=3, seed=97 + d)
+    b = synth.make_batch(wl)
+    extra = 17300 - b.block_table.shape[1]
+    b.block_table = np.ascontiguousarray(
+        np.concatenate([b.block_table, np.repeat(b.block_table[:, :1], extra, axis=1)], axis=1))
+    _forward_case(wl, batch=b)
+
+
 def test_forward_gptoss_c1_full():
     _forward_case(synth.WORKLOADS["gptoss20b-bf16-c1-k7"])
 
