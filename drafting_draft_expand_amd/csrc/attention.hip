@@ -493,8 +493,8 @@ __global__ __launch_bounds__(512, D == 64 ? 4 : 2) void attn_ring_kernel(AttnArg
     const int off = (p % BS) * D + cgc * 8;
 #pragma unroll
     for (int pl = 0; pl < PL; ++pl) {
-      dma16(kc + base + off + pl * 64, st + pl * SP + wave * 8 * 64);
-      dma16(vc + base + off + pl * 64, st + SK + pl * SP + wave * 8 * 64);
+      dma16<true>(kc + base + off + pl * 64, st + pl * SP + wave * 8 * 64);
+      dma16<true>(vc + base + off + pl * 64, st + SK + pl * SP + wave * 8 * 64);
     }
   };
   constexpr int kWait = waitcnt_vm_lgkm0((ST - 2) * 2 * PL);

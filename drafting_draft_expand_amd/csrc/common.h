@@ -125,12 +125,18 @@ __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u3
 // the compiler's own wait-count bookkeeping, which cannot tell ring stages
 // apart and would wait for every copy before the next LDS read, leaves these
 // copies alone: the kernel waits for them itself.  M0 holds the LDS address
-// and needs one wait state before the copy reads it.
+// and needs one wait state before the copy reads it.  STREAM marks the read
+// non-temporal (data read once, e.g. the KV cache), so it does not displace
+// data that is reused from the caches.
+template <bool STREAM = false>
 __device__ __forceinline__ void dma16(const void* g, void* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const unsigned m = __builtin_amdgcn_readfirstlane(
       static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds)));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(m) : "memory", "m0");
+  if constexpr (STREAM)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(g), "s"(m) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(m) : "memory", "m0");
 #endif
 }
 
