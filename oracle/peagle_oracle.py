@@ -24,7 +24,10 @@ float64.  ``precision="mirror"`` rounds to the storage dtype exactly at the
 points where the HIP path stores a tensor or feeds a matrix operand (KV cache
 entries, the normalised activations, q, the attention output, SiLU(gate)*up,
 the final normalised rows); everything else stays float64.
-``precision="fp64"`` never rounds.  parity: pinned by tests/test_oracle_*.py.
+``precision="fp64"`` never rounds.  parity: pinned by tests/test_oracle_*.py
+(the bf16 codec bit for bit against torch's cast over every pattern and tie,
+the mirror rounding points against a torch composition that rounds at exactly
+those points, each point shown to be observable).
 """
 
 from __future__ import annotations
@@ -242,16 +245,18 @@ def paged_attention(q: np.ndarray, q_pos: np.ndarray, keys: np.ndarray, values: 
     rows, n_q, d = q.shape
     n_kv = keys.shape[1]
     grp = n_q // n_kv
-    kh = np.repeat(keys, grp, axis=1)            # [kv_len, n_q, d]
-    vh = np.repeat(values, grp, axis=1)
-    scores = np.einsum("rhd,jhd->rhj", q, kh) / np.sqrt(d)
+    # per query head h: its kv head's keys and values (head-major for matmul)
+    kh = np.repeat(keys, grp, axis=1).transpose(1, 2, 0)      # [n_q, d, kv_len]
+    vh = np.repeat(values, grp, axis=1).transpose(1, 0, 2)    # [n_q, kv_len, d]
+    qh = q.transpose(1, 0, 2)                                  # [n_q, rows, d]
+    scores = np.matmul(qh, kh) / np.sqrt(d)                    # [n_q, rows, kv_len]
     kpos = np.arange(keys.shape[0])
-    visible = kpos[None, None, :] <= np.asarray(q_pos)[:, None, None]
+    visible = kpos[None, None, :] <= np.asarray(q_pos)[None, :, None]
     scores = np.where(visible, scores, -np.inf)
     m = np.max(scores, axis=-1, keepdims=True)
     e = np.exp(scores - m)
     w = e / np.sum(e, axis=-1, keepdims=True)
-    return np.einsum("rhj,jhd->rhd", w, vh)
+    return np.matmul(w, vh).transpose(1, 0, 2)                 # [rows, n_q, d]
 
 
 def _slots_of(block_table_row: np.ndarray, positions: np.ndarray, block_size: int) -> np.ndarray:
