@@ -160,7 +160,7 @@ def _bench_prep(args) -> int:
     for _ in range(args.warmup):
         step()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    model.timing_enable(pe.PE_KERNEL_PREPARE, True)
+    pe.timing_enable(pe.PE_KERNEL_PREPARE, True)
     torch.cuda.synchronize()
     start.record(stream)
     for _ in range(args.steps):
@@ -168,8 +168,8 @@ def _bench_prep(args) -> int:
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    k_ms, k_n = model.timing_read(pe.PE_KERNEL_PREPARE)
-    model.timing_enable(pe.PE_KERNEL_PREPARE, False)
+    k_ms, k_n, _ = pe.timing_read(pe.PE_KERNEL_PREPARE)
+    pe.timing_enable(pe.PE_KERNEL_PREPARE, False)
     k_s = k_ms / max(k_n, 1) / 1e3
     nbytes = prep_bytes(spec, b, K)
     gbs = nbytes / (ms / 1e3) / 1e9
@@ -312,10 +312,10 @@ def main() -> int:
     # timed with HIP events on its own stream over these steps
     for _ in range(args.warmup):
         step()
-    model.timing_enable(pe.PE_KERNEL_LM_HEAD, True)
+    pe.timing_enable(pe.PE_KERNEL_LM_HEAD, True)
     eager_ms = timed(step, args.steps)
-    lm_ms, lm_n = model.timing_read(pe.PE_KERNEL_LM_HEAD)
-    model.timing_enable(pe.PE_KERNEL_LM_HEAD, False)
+    lm_ms, lm_n, _ = pe.timing_read(pe.PE_KERNEL_LM_HEAD)
+    pe.timing_enable(pe.PE_KERNEL_LM_HEAD, False)
     ms_per_step, mode = eager_ms, "eager"
     graph_ms = None
     if not args.eager and args.mode == "peagle":

@@ -22,6 +22,8 @@ from ._lib import (  # noqa: F401
     next_verified_batch,
     prepare_draft_batch,
     status_string,
+    timing_enable,
+    timing_read,
     PE_KERNEL_LM_HEAD,
     PE_KERNEL_PREPARE,
     PE_KERNEL_ATTENTION,

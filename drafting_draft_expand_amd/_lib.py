@@ -86,13 +86,13 @@ def load() -> ctypes.CDLL:
     lib.pe_accept.restype = I32
     lib.pe_status_string.argtypes = [I32]
     lib.pe_status_string.restype = ctypes.c_char_p
-    lib.pe_timing_enable.argtypes = [P, I32, I32]
+    lib.pe_timing_enable.argtypes = [I32, I32]
     lib.pe_timing_enable.restype = I32
-    lib.pe_timing_read.argtypes = [P, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]
+    lib.pe_timing_read.argtypes = [I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64), P, I64]
     lib.pe_timing_read.restype = I32
     lib.pe_autoregressive_workspace_bytes.argtypes = [P, I32, I32, I32]
     lib.pe_autoregressive_workspace_bytes.restype = SZ
-    lib.pe_draft_autoregressive.argtypes = [P, I32, I32, I32] + [P] * 7 + [I32] + [P, P, P, SZ, P, P]
+    lib.pe_draft_autoregressive.argtypes = [P, I32, I32, I32] + [P] * 7 + [I32] + [P, P, P, SZ, P, P, P, P]
     lib.pe_draft_autoregressive.restype = I32
     lib.pe_next_verified_batch.argtypes = [I32, I32] + [P] * 10 + [P]
     lib.pe_next_verified_batch.restype = I32
@@ -171,14 +171,6 @@ class DraftModel:
     def autoregressive_workspace_bytes(self, num_seqs: int, K: int, total_target_rows: int) -> int:
         return int(load().pe_autoregressive_workspace_bytes(self.handle, num_seqs, K, total_target_rows))
 
-    def timing_enable(self, kernel: int, enable: bool = True) -> None:
-        _check(load().pe_timing_enable(self.handle, kernel, int(enable)), "pe_timing_enable")
-
-    def timing_read(self, kernel: int):
-        ms, n = ctypes.c_double(), ctypes.c_int64()
-        _check(load().pe_timing_read(self.handle, kernel, ctypes.byref(ms), ctypes.byref(n)), "pe_timing_read")
-        return ms.value, n.value
-
     def close(self) -> None:
         if getattr(self, "handle", None):
             load().pe_model_destroy(self.handle)
@@ -189,6 +181,22 @@ class DraftModel:
             self.close()
         except Exception:
             pass
+
+
+def timing_enable(kernel: int, enable: bool = True) -> None:
+    """Start (or stop) recording launch times of a kernel class (see pe_timing_enable)."""
+    _check(load().pe_timing_enable(kernel, int(enable)), "pe_timing_enable")
+
+
+def timing_read(kernel: int):
+    """(total ms, launches, per-launch ms list) recorded since timing_enable (see pe_timing_read)."""
+    lib = load()
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(lib.pe_timing_read(kernel, ctypes.byref(ms), ctypes.byref(n), None, 0), "pe_timing_read")
+    per = (ctypes.c_float * max(1, n.value))()
+    _check(lib.pe_timing_read(kernel, ctypes.byref(ms), ctypes.byref(n), ctypes.cast(per, ctypes.c_void_p),
+                              n.value), "pe_timing_read")
+    return ms.value, n.value, list(per[:n.value])
 
 
 def prepare_draft_batch(model: DraftModel, K: int, query_lens: torch.Tensor, target_ids: torch.Tensor,
@@ -266,8 +274,11 @@ def draft_autoregressive(model: DraftModel, K: int, query_lens: torch.Tensor, ta
                          target_pos: torch.Tensor, num_accepted: torch.Tensor, bonus_ids: torch.Tensor,
                          target_hidden: torch.Tensor, block_table: torch.Tensor, k_cache: Sequence[torch.Tensor],
                          v_cache: Sequence[torch.Tensor], workspace: Optional[torch.Tensor] = None,
-                         tokens: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """K sequential one-token drafter passes (see pe_draft_autoregressive).  Returns tokens [c, K] (int32)."""
+                         tokens: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+                         fed_hidden: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """K sequential one-token drafter passes (see pe_draft_autoregressive).  Returns tokens [c, K] (int32);
+    ``logits`` (optional float32 [K, c, V]) receives each pass's logits, ``fed_hidden`` (optional
+    [K-1, c, H], model dtype) the hidden input of passes 1..K-1."""
     c = int(query_lens.numel())
     T = int(target_ids.numel())
     dev = target_ids.device
@@ -281,7 +292,8 @@ def draft_autoregressive(model: DraftModel, K: int, query_lens: torch.Tensor, ta
         model.handle, c, K, T, _ptr(query_lens), _ptr(target_ids), _ptr(target_pos), _ptr(num_accepted),
         _ptr(bonus_ids), _ptr(target_hidden), _ptr(block_table), int(block_table.shape[1]),
         ctypes.cast(kp, ctypes.c_void_p), ctypes.cast(vp, ctypes.c_void_p), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _ptr(tokens), _stream(stream))
+        workspace.numel() * workspace.element_size(), _ptr(tokens), _ptr(logits), _ptr(fed_hidden),
+        _stream(stream))
     _check(st, "pe_draft_autoregressive")
     return tokens
 

@@ -4,8 +4,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <utility>
 #include <vector>
@@ -16,11 +18,18 @@ using pe::DType;
 
 namespace {
 
+// Kernel timing for measurement harnesses: one process-wide record per kernel
+// class, guarded by a mutex, so that the model handles stay read-only after
+// set-up.  The event pairs are created on first use and reused until the
+// process ends.
 struct Timing {
-  bool enabled = false;
+  std::atomic<bool> enabled{false};
   std::vector<std::pair<hipEvent_t, hipEvent_t>> events;  // recorded pairs
   size_t used = 0;
 };
+constexpr int kTimingClasses = 3;
+std::mutex g_timing_mu;
+Timing g_timing[kTimingClasses];
 
 }  // namespace
 
@@ -37,9 +46,8 @@ struct pe_model {
   const void* pk_fc = nullptr;
   std::vector<PackedLayer> pk_layers;  // empty: not packed
   const void* pk_lm = nullptr;         // tile-major LM head (packed models)
-  int num_cus = 0;  // queried on first launch
+  int num_cus = 256;  // compute units of the device current at create
   pe::RopeFreq freq; // theta^(-2j/d) in double precision
-  Timing timing[3];
 };
 
 namespace {
@@ -141,24 +149,29 @@ bool fused_final_norm(const pe_model_desc& d, int N, int S) {
          pe::proj_kernel(S, d.hidden, t) != pe::ProjKernel::Tiled;
 }
 
-int num_cus(pe_model* m) {
-  if (m->num_cus > 0) return m->num_cus;
+// Compute units of the current device (256 if the runtime cannot say, e.g.
+// on a host without a GPU, where nothing is launched anyway).
+int query_num_cus() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) == hipSuccess &&
       hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-    m->num_cus = n;
-  else
-    m->num_cus = 256;
-  return m->num_cus;
+    return n;
+  (void)hipGetLastError();  // leave no sticky error behind
+  return 256;
 }
 
-// Optional event pair around one launch of a timed kernel class.
+// Optional event pair around one launch of a timed kernel class; while the
+// class is enabled the scope holds the timing lock, so concurrent callers
+// record their pairs one after the other.
 struct TimedScope {
   Timing* t;
   hipStream_t s;
   hipEvent_t stop = nullptr;
-  TimedScope(pe_model* m, pe_kernel_class k, hipStream_t stream) : t(&m->timing[k]), s(stream) {
-    if (!t->enabled) { t = nullptr; return; }
+  std::unique_lock<std::mutex> lock;
+  TimedScope(pe_kernel_class k, hipStream_t stream) : t(&g_timing[k]), s(stream) {
+    if (!t->enabled.load(std::memory_order_relaxed)) { t = nullptr; return; }
+    lock = std::unique_lock<std::mutex>(g_timing_mu);
+    if (!t->enabled.load(std::memory_order_relaxed)) { t = nullptr; return; }
     if (t->used == t->events.size()) {
       hipEvent_t a, b;
       if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) { t = nullptr; return; }
@@ -222,19 +235,12 @@ pe_status pe_model_create(const pe_model_desc* desc, const pe_weights* w, pe_mod
                          ? std::pow(static_cast<double>(desc->rope_theta), -2.0 * j / desc->head_dim)
                          : 0.0;
   m->w.layers = m->layers.empty() ? nullptr : m->layers.data();
+  m->num_cus = query_num_cus();
   *out = m;
   return PE_OK;
 }
 
-void pe_model_destroy(pe_model* m) {
-  if (!m) return;
-  for (auto& t : m->timing)
-    for (auto& e : t.events) {
-      (void)hipEventDestroy(e.first);
-      (void)hipEventDestroy(e.second);
-    }
-  delete m;
-}
+void pe_model_destroy(pe_model* m) { delete m; }
 
 namespace {
 // The matrices the weight-streaming kernel reads, in buffer order: fc, then
@@ -335,7 +341,7 @@ pe_status prepare_impl(const pe_model* m, int32_t c, int32_t K, int32_t T, const
   a.is_rejected = is_rejected; a.is_masked = is_masked; a.hidden_map = hidden_map;
   a.cu_draft = cu_draft; a.kv_lens = kv_lens; a.sample_idx = sample_idx; a.draft_hidden = draft_hidden;
   a.compact = compact;
-  TimedScope ts(const_cast<pe_model*>(m), PE_KERNEL_PREPARE, stream);
+  TimedScope ts(PE_KERNEL_PREPARE, stream);
   PE_HIP(pe::launch_prepare(a, stream));
   return PE_OK;
 }
@@ -396,7 +402,7 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
                            const int32_t* block_table, int32_t max_blocks, void* const* k_cache,
                            void* const* v_cache, void* workspace, size_t workspace_bytes,
                            int32_t* draft_tokens, float* logits, float* top2_gap, hipStream_t stream) {
-  pe_model* m = const_cast<pe_model*>(mc);
+  const pe_model* m = mc;  // read only: the handle is shared by every stream and thread
   if (!m || c <= 0 || K <= 0 || N < c * K || max_blocks <= 0) return PE_EINVAL;
   if (m->d.n_layers <= 0) return PE_EUNSUPPORTED;
   const void* ptrs[] = {draft_ids, draft_pos, slot_mapping, is_rejected, cu_draft, kv_lens,
@@ -431,7 +437,7 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
   void* f = wb + ws.f;
   float* ss0 = reinterpret_cast<float*>(wb + ws.ss0);
   float* xpart = reinterpret_cast<float*>(wb + ws.part);
-  const int cus = num_cus(m);
+  const int cus = m->num_cus;
 
   const int ss_tiles = (H + 15) / 16;
   // rows at and past cu_draft[c] are padding (compacted layout): skipped
@@ -449,7 +455,7 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
     at.q = qrot; at.pos = draft_pos; at.rejected = is_rejected; at.cu_draft = cu_draft;
     at.kv_lens = kv_lens; at.block_table = block_table; at.k_cache = k_cache[l];
     at.v_cache = v_cache[l]; at.partial = part; at.out = act;
-    TimedScope ts(m, PE_KERNEL_ATTENTION, stream);
+    TimedScope ts(PE_KERNEL_ATTENTION, stream);
     PE_HIP(pe::launch_attention(at, stream));
     return PE_OK;
   };
@@ -615,7 +621,7 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
     g.logits = logits; g.partials = top2;
     if (pe::gemv_grid_x(S, d.vocab, pe::Epi::Argmax, t, cus, H) > ws.lm_parts) return PE_EUNSUPPORTED;
     {
-      TimedScope ts(m, PE_KERNEL_LM_HEAD, stream);
+      TimedScope ts(PE_KERNEL_LM_HEAD, stream);
       if ((st = proj(g, pe::Epi::Argmax)) != PE_OK) return st;
     }
     PE_HIP(pe::launch_argmax_finalize(S, g.grid_x, top2, draft_tokens, top2_gap, stream));
@@ -685,10 +691,11 @@ pe_status pe_draft_autoregressive(const pe_model* m, int32_t c, int32_t K, int32
                                   const int32_t* bonus_ids, const void* target_hidden,
                                   const int32_t* block_table, int32_t max_blocks, void* const* k_cache,
                                   void* const* v_cache, void* workspace, size_t workspace_bytes,
-                                  int32_t* draft_tokens, hipStream_t stream) {
+                                  int32_t* draft_tokens, float* logits, void* fed_hidden, hipStream_t stream) {
   if (!m || c <= 0 || K <= 0 || T < c || max_blocks <= 0 || !workspace || !draft_tokens) return PE_EINVAL;
   if (m->d.n_layers <= 0) return PE_EUNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return PE_EINVAL;
+  if (fed_hidden && !aligned16(fed_hidden)) return PE_EINVAL;
   const ArWorkspace ws = plan_ar(m, c, T);
   if (workspace_bytes < ws.total) return PE_EWORKSPACE;
   char* wb = static_cast<char*>(workspace);
@@ -704,22 +711,26 @@ pe_status pe_draft_autoregressive(const pe_model* m, int32_t c, int32_t K, int32
     return st;
   if ((st = pe_draft_forward(m, c, 1, T, m1.ids, m1.pos, m1.slot, m1.rej, m1.cu, m1.kvl, m1.sidx,
                              wb + ws.hid1, block_table, max_blocks, k_cache, v_cache, fwd, ws.fwd_bytes, tok,
-                             nullptr, nullptr, stream)) != PE_OK)
+                             logits, nullptr, stream)) != PE_OK)
     return st;
   // passes 2..K: one row per sequence fed with its own previous token and
   // final residual (the drafter workspace's residual region sits at offset 0)
+  const size_t hid_bytes = size_t(c) * m->d.hidden * (m->d.dtype == PE_F32 ? 4 : 2);
   for (int k = 1; k <= K; ++k) {
+    // hidden rows of pass k: the caller's buffer when given, else scratch
+    void* hid = fed_hidden && k < K ? static_cast<char*>(fed_hidden) + (k - 1) * hid_bytes : wb + ws.hidk;
     pe::ArStepArgs a{};
     a.c = c; a.K = K; a.k = k; a.H = m->d.hidden; a.max_blocks = max_blocks; a.last = k == K;
     a.dtype = dt(m); a.prev_tokens = tok; a.x = reinterpret_cast<const float*>(fwd);
     a.prev_sample_idx = k == 1 ? m1.sidx : nullptr; a.base_kv_lens = m1.kvl; a.block_table = block_table;
     a.draft_tokens = draft_tokens; a.ids = mk.ids; a.pos = mk.pos; a.slot = mk.slot; a.rejected = mk.rej;
-    a.cu_draft = mk.cu; a.kv_lens = mk.kvl; a.sample_idx = mk.sidx; a.hidden = wb + ws.hidk;
+    a.cu_draft = mk.cu; a.kv_lens = mk.kvl; a.sample_idx = mk.sidx; a.hidden = hid;
     PE_HIP(pe::launch_ar_step(a, stream));
     if (k == K) break;
     if ((st = pe_draft_forward(m, c, 1, c, mk.ids, mk.pos, mk.slot, mk.rej, mk.cu, mk.kvl, mk.sidx,
-                               wb + ws.hidk, block_table, max_blocks, k_cache, v_cache, fwd, ws.fwd_bytes, tok,
-                               nullptr, nullptr, stream)) != PE_OK)
+                               hid, block_table, max_blocks, k_cache, v_cache, fwd, ws.fwd_bytes, tok,
+                               logits ? logits + static_cast<size_t>(k) * c * m->d.vocab : nullptr, nullptr,
+                               stream)) != PE_OK)
       return st;
   }
   return PE_OK;
@@ -748,21 +759,26 @@ pe_status pe_accept(int32_t c, int32_t K, const int32_t* draft, const int32_t* t
   return PE_OK;
 }
 
-pe_status pe_timing_enable(pe_model* m, pe_kernel_class k, int32_t enable) {
-  if (!m || k < PE_KERNEL_LM_HEAD || k > PE_KERNEL_ATTENTION) return PE_EINVAL;
-  m->timing[k].enabled = enable != 0;
-  m->timing[k].used = 0;
+pe_status pe_timing_enable(pe_kernel_class k, int32_t enable) {
+  if (k < PE_KERNEL_LM_HEAD || k > PE_KERNEL_ATTENTION) return PE_EINVAL;
+  std::lock_guard<std::mutex> g(g_timing_mu);
+  g_timing[k].enabled.store(enable != 0, std::memory_order_relaxed);
+  g_timing[k].used = 0;
   return PE_OK;
 }
 
-pe_status pe_timing_read(pe_model* m, pe_kernel_class k, double* total_ms, int64_t* launches) {
-  if (!m || !total_ms || !launches || k < PE_KERNEL_LM_HEAD || k > PE_KERNEL_ATTENTION) return PE_EINVAL;
-  Timing& t = m->timing[k];
+pe_status pe_timing_read(pe_kernel_class k, double* total_ms, int64_t* launches, float* per_launch_ms,
+                         int64_t capacity) {
+  if (!total_ms || !launches || k < PE_KERNEL_LM_HEAD || k > PE_KERNEL_ATTENTION) return PE_EINVAL;
+  if (per_launch_ms && capacity < 0) return PE_EINVAL;
+  std::lock_guard<std::mutex> g(g_timing_mu);
+  Timing& t = g_timing[k];
   double sum = 0.0;
   for (size_t i = 0; i < t.used; ++i) {
     PE_HIP(hipEventSynchronize(t.events[i].second));
     float ms = 0.f;
     PE_HIP(hipEventElapsedTime(&ms, t.events[i].first, t.events[i].second));
+    if (per_launch_ms && static_cast<int64_t>(i) < capacity) per_launch_ms[i] = ms;
     sum += ms;
   }
   *total_ms = sum;

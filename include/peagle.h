@@ -108,10 +108,17 @@ typedef struct {
   const pe_layer_weights *layers;
 } pe_weights;
 
-typedef struct pe_model pe_model; /* opaque; usable from any stream once created (and packed) */
+/* Opaque drafter handle.  Set-up is pe_model_create followed, optionally, by
+ * pe_model_pack_weights; those two are the only calls that modify the handle.
+ * After set-up it is read-only: every other call takes it as const, and
+ * concurrent calls from several host threads on several streams may share it
+ * (each with its own workspace and outputs). */
+typedef struct pe_model pe_model;
 
 /* Validate the description and weight pointers and build a model handle
- * (host memory only).  Returns PE_EINVAL / PE_EUNSUPPORTED on bad input. */
+ * (host memory only; the compute-unit count of the current HIP device is
+ * recorded for launch shapes).  Returns PE_EINVAL / PE_EUNSUPPORTED on bad
+ * input. */
 pe_status pe_model_create(const pe_model_desc *desc, const pe_weights *weights, pe_model **out);
 void pe_model_destroy(pe_model *model);
 
@@ -122,7 +129,7 @@ void pe_model_destroy(pe_model *model);
  * multiples of 32 or head_dim not a multiple of 16). */
 size_t pe_packed_weights_bytes(const pe_model *model);
 
-/* Optional, for speed.  Copies the projection weights into `packed` in the
+/* Optional part of set-up, for speed.  Copies the projection weights into `packed` in the
  * fragment order of the bf16 matrix-core tiles (each 16-output x 32-input
  * fragment one contiguous KiB, the q/k/v rows grouped in rotary pairs), read
  * with few draft rows (at most 16 rows per pass, e.g. one sequence at K <= 8),
@@ -136,6 +143,11 @@ size_t pe_packed_weights_bytes(const pe_model *model);
  * they are when the copy runs on `stream` (later changes to the row-major
  * weights are not seen).  Forward calls on other streams must be ordered after
  * that work; do not call it while a pass using the model is in flight.
+ * Memory cost: the copies add to the caller's row-major weights, which stay
+ * in use (the LM head over at most 16 sampled rows, the embedding, the norms);
+ * for a GPT-OSS-20B-shaped drafter (hidden 2880, vocab 201088) that is
+ * 219 MB of projections plus 1.16 GB for the LM head, so the drafter's weight
+ * footprint grows from 1.38 GB to about 2.76 GB.
  * Returns PE_OK (nothing to do when 0 bytes are needed), PE_EINVAL (null or
  * misaligned buffer), PE_EWORKSPACE (too small), PE_EHIP. */
 pe_status pe_model_pack_weights(pe_model *model, void *packed, size_t packed_bytes, hipStream_t stream);
@@ -259,6 +271,12 @@ pe_status pe_accept(int32_t num_seqs, int32_t K, const int32_t *draft_tokens,
  *   workspace: device scratch of at least pe_autoregressive_workspace_bytes(
  *              model, c, K, T) bytes, 256-byte aligned
  *   draft_tokens[c*K]  int32 output, sequence-major
+ *   logits_or_null     optional float32 [K, c, V], step-major: row (k, i) holds
+ *                      the logits that gave token k of sequence i
+ *   fed_hidden_or_null optional [K-1, c, H] model dtype, 16-byte aligned:
+ *                      receives the hidden input of pass k = 1..K-1 (row
+ *                      (k-1, i): sequence i's rounded final residual fed back);
+ *                      when given, the passes read their hidden rows from it
  * Returns PE_EWORKSPACE for a short workspace; otherwise as pe_draft_forward.
  * Launches K forward passes plus small row builders on the stream; nothing is
  * synchronized on the host.
@@ -272,7 +290,7 @@ pe_status pe_draft_autoregressive(const pe_model *model, int32_t num_seqs, int32
                                   const void *target_hidden, const int32_t *block_table,
                                   int32_t max_blocks, void *const *k_cache, void *const *v_cache,
                                   void *workspace, size_t workspace_bytes, int32_t *draft_tokens,
-                                  hipStream_t stream);
+                                  float *logits_or_null, void *fed_hidden_or_null, hipStream_t stream);
 
 /* Next round's verified batch, on the device ("P-EAGLE: Faster LLM Inference
  * with Parallel Speculative Decoding in vLLM", 怎么做的: each round drafts K
@@ -327,14 +345,19 @@ pe_status pe_check_verified_batch(const pe_model *model, int32_t num_seqs, int32
 /* Static description of a status code. */
 const char *pe_status_string(pe_status status);
 
-/* Kernel timing for measurement harnesses.  While enabled for a kernel class,
- * every launch of that class records a pair of HIP events on the stream it is
- * launched on; pe_timing_read synchronizes on the recorded events and returns
- * the summed elapsed milliseconds and the number of launches since enable.
- * Not thread-safe against concurrent forward calls on the same model. */
+/* Kernel timing for measurement harnesses (process-wide, not part of any
+ * model).  While enabled for a kernel class, every launch of that class, from
+ * any model, thread or stream, records a pair of HIP events on the stream it
+ * is launched on; enabling (or re-enabling) discards earlier records.
+ * pe_timing_read synchronizes on the recorded events and returns the summed
+ * elapsed milliseconds and the number of launches since enable, and, when
+ * per_launch_ms is given, the first `capacity` launch times in launch order.
+ * Thread-safe; while a class is enabled its launches are serialized on the
+ * host.  Do not enable timing while a stream is being captured into a graph. */
 typedef enum { PE_KERNEL_LM_HEAD = 0, PE_KERNEL_PREPARE = 1, PE_KERNEL_ATTENTION = 2 } pe_kernel_class;
-pe_status pe_timing_enable(pe_model *model, pe_kernel_class kernel, int32_t enable);
-pe_status pe_timing_read(pe_model *model, pe_kernel_class kernel, double *total_ms, int64_t *launches);
+pe_status pe_timing_enable(pe_kernel_class kernel, int32_t enable);
+pe_status pe_timing_read(pe_kernel_class kernel, double *total_ms, int64_t *launches, float *per_launch_ms,
+                         int64_t capacity);
 
 #ifdef __cplusplus
 }

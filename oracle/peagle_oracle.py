@@ -441,7 +441,8 @@ def next_verified_batch(kv_lens, bonus_ids, draft_tokens, num_accepted_next, bon
 # autoregressive baseline
 # ----------------------------------------------------------------------------
 def autoregressive_draft(spec, weights: dict, batch, K: int, precision: str = "mirror",
-                         seqs: Optional[Sequence[int]] = None, forced_tokens: Optional[np.ndarray] = None) -> dict:
+                         seqs: Optional[Sequence[int]] = None, forced_tokens: Optional[np.ndarray] = None,
+                         forced_hidden: Optional[np.ndarray] = None) -> dict:
     """K drafts from K sequential one-token passes, the drafting scheme whose
     latency grows with K ([PP] "Solving the Autoregressive Drafting
     Bottleneck").
@@ -456,8 +457,11 @@ def autoregressive_draft(spec, weights: dict, batch, K: int, precision: str = "m
     are committed before the next pass.
 
     ``forced_tokens`` [c, K] feeds those tokens forward instead of the
-    oracle's own argmax (teacher forcing against another implementation's
-    drafts).  Returns tokens and logits per step and the final caches.
+    oracle's own argmax, and ``forced_hidden`` [K-1, c, H] (storage dtype)
+    those hidden rows instead of the oracle's own rounded residuals (teacher
+    forcing against another implementation's drafts and fed-back states).
+    Returns tokens and logits per step, the hidden rows the oracle itself
+    would feed back ([K-1, len(seqs), H], storage dtype) and the final caches.
     """
     dt = spec.dtype
     c = len(batch.query_lens)
@@ -472,6 +476,7 @@ def autoregressive_draft(spec, weights: dict, batch, K: int, precision: str = "m
     base = np.asarray(meta["kv_lens"], dtype=np.int64) - 1
     tokens = np.zeros((len(seqs), K), np.int64)
     logits = []
+    own_hidden = []
     for k in range(K):
         f = draft_forward(spec, weights, meta, hd, batch.block_table, kc, vc, 1, precision=precision, seqs=seqs)
         apply_cache_writes(spec, kc, vc, f["cache_writes"])
@@ -485,7 +490,8 @@ def autoregressive_draft(spec, weights: dict, batch, K: int, precision: str = "m
         ids = np.zeros(c, np.int32)
         hid = np.zeros((c, spec.hidden), dtype=np.uint16 if dt == "bf16" else np.float32)
         ids[seqs] = feed
-        hid[seqs] = encode(xs, dt)
+        own_hidden.append(encode(xs, dt))
+        hid[seqs] = own_hidden[-1] if forced_hidden is None else np.asarray(forced_hidden)[k][seqs]
         pos = (base + k + 1).astype(np.int32)
         slot = np.array([_slots_of(np.asarray(batch.block_table[i], dtype=np.int64), np.array([pos[i]]),
                                    spec.block_size)[0] for i in range(c)], dtype=np.int64)
@@ -493,7 +499,10 @@ def autoregressive_draft(spec, weights: dict, batch, K: int, precision: str = "m
                     is_masked=np.zeros(c, np.uint8), cu_draft=np.arange(c + 1, dtype=np.int32),
                     kv_lens=(pos.astype(np.int64) + 1).astype(np.int32), sample_idx=np.arange(c, dtype=np.int32))
         hd = hid
-    return dict(tokens=tokens, logits=np.stack(logits, axis=1), k_cache=kc, v_cache=vc, seqs=np.array(seqs))
+    hdt = np.uint16 if dt == "bf16" else np.float32
+    fed = np.stack(own_hidden) if own_hidden else np.zeros((0, len(seqs), spec.hidden), hdt)
+    return dict(tokens=tokens, logits=np.stack(logits, axis=1), fed_hidden=fed, k_cache=kc, v_cache=vc,
+                seqs=np.array(seqs))
 
 
 # ----------------------------------------------------------------------------

@@ -127,3 +127,47 @@ def test_expansion_only_model_refuses_forward(lib):
                                        0x40000, 1 << 30, P, None, None, None]
     assert lib.pe_draft_forward(*fargs) == -2
     lib.pe_model_destroy(h)
+
+
+def test_forward_validation_from_two_threads(lib):
+    """The handle is read-only after set-up: two host threads validating
+    forward calls on the same model at once see the same statuses (no launch
+    happens: every call fails a host check first)."""
+    import threading
+    st, h = _create(lib, _desc())
+    assert st == 0
+    P = 0x20000
+    kp = (ctypes.c_void_p * 1)(P)
+    need = lib.pe_workspace_bytes(h, 2, 3, 12)
+    short = [h, 2, 3, 12] + [P] * 9 + [1, ctypes.cast(kp, ctypes.c_void_p), ctypes.cast(kp, ctypes.c_void_p),
+                                       0x40000, need - 1, P, None, None, None]
+    bad_n = list(short)
+    bad_n[3] = 5
+    results = [[], []]
+
+    def work(slot):
+        for _ in range(2000):
+            results[slot].append((lib.pe_draft_forward(*short), lib.pe_draft_forward(*bad_n),
+                                  lib.pe_workspace_bytes(h, 2, 3, 12)))
+
+    try:
+        ts = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+        for r in results:
+            assert len(r) == 2000 and set(r) == {(-3, -1, need)}
+    finally:
+        lib.pe_model_destroy(h)
+
+
+def test_timing_api_without_launches(lib):
+    from drafting_draft_expand_amd import _lib
+    for k in (_lib.PE_KERNEL_LM_HEAD, _lib.PE_KERNEL_PREPARE, _lib.PE_KERNEL_ATTENTION):
+        _lib.timing_enable(k, True)
+        assert _lib.timing_read(k) == (0.0, 0, [])
+        _lib.timing_enable(k, False)
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    assert lib.pe_timing_read(7, ctypes.byref(ms), ctypes.byref(n), None, 0) == -1
+    assert lib.pe_timing_enable(-1, 1) == -1

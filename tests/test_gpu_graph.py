@@ -4,17 +4,23 @@ The round (prepare_draft_batch -> draft_forward -> accept) is captured once at
 fixed shapes and replayed, the deployment form of the CUDA-graph capture the
 pages describe ("P-EAGLE: Parallel Speculative Decoding in vLLM", KV Cache and
 CUDA Graphs).  Every replay must reproduce the eager round exactly, also with
-unrelated eager work and synchronisations between the replays.
+unrelated eager work and synchronisations between the replays, and the
+replayed round is checked against the oracle: expansion and placed hidden
+rows bit-exact, every token an oracle argmax up to the logit tolerance, every
+KV entry the round writes equal to the oracle's (unwritten slots untouched),
+acceptance equal to the oracle's on the replayed drafts.
 """
 
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
 from synth.device import from_torch, to_torch, upload_batch
 
-from gpu_harness import DEV, device_model, _say
+from gpu_harness import (DEV, LOGIT_TOL, _say, check_cache, check_prepare_exact, check_tokens, device_model,
+                         host_weights)
 
 pytestmark = pytest.mark.gpu
 
@@ -26,7 +32,8 @@ def _round(pe, model, db, K, prep, ws, tokens, tgt, acc, bonus):
     pe.accept(tokens, tgt, acc, bonus)
 
 
-@pytest.mark.parametrize("name", ["tiny-fp32-c2-k3", "qwen3coder30b-bf16-c16-k5"])
+@pytest.mark.parametrize("name", ["tiny-fp32-c2-k3", "qwen3coder30b-bf16-c16-k5", "gptoss20b-bf16-c1-k7",
+                                  "gptoss20b-bf16-c64-k7"])
 def test_graph_replay_matches_eager(name):
     import drafting_draft_expand_amd as pe
     wl = synth.WORKLOADS[name]
@@ -74,4 +81,18 @@ def test_graph_replay_matches_eager(name):
             assert np.array_equal(from_torch(v), ref[k]), f"replay {rep}: {k} differs from the eager round"
         for got, want in zip((from_torch(k) for k in db["k_cache"]), ref_k):
             assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), f"replay {rep}: KV cache differs"
-    _say("  4 replays identical to the eager round")
+    _say("  4 replays identical to the eager round; oracle")
+    spec = wl.model
+    w = host_weights(spec, wl.wseed)
+    ref = oracle.parallel_draft_step(spec, w, b, precision="mirror")
+    check_prepare_exact(prep, ref["meta"], ref["draft_hidden"])
+    fw = ref["forward"]
+    tol = LOGIT_TOL[spec.dtype]
+    g_tok = from_torch(tokens).astype(np.int64)
+    exact = check_tokens(g_tok.reshape(-1), fw["logits"].reshape(c * K, -1), tol)
+    check_cache(spec, b.k_cache, b.v_cache, [from_torch(k) for k in db["k_cache"]],
+                [from_torch(v) for v in db["v_cache"]], from_torch(prep["slot_mapping"]), fw["cache_writes"],
+                spec.dtype)
+    oa, ob = oracle.accept(g_tok, from_torch(tgt))
+    assert np.array_equal(from_torch(acc), oa) and np.array_equal(from_torch(bonus), ob)
+    _say(f"  replayed round vs oracle: tokens identical to its argmax {exact:.3f}, cache and acceptance equal")

@@ -225,3 +225,21 @@ def test_apply_cache_writes_stores_exactly_the_writes():
     for sl in slots:
         mask[sl // 16, :, sl % 16] = False
     np.testing.assert_array_equal(kc[0][mask], before[mask])
+
+
+def test_forced_hidden_rows_feed_the_given_states():
+    """Forcing the oracle's own fed-back rows reproduces its free run exactly;
+    forcing different rows changes every later pass but not the first."""
+    spec, w, b = _tiny_ar_case(K=3, seed=65)
+    own = oracle.autoregressive_draft(spec, w, b, 3, precision="mirror")
+    assert own["fed_hidden"].shape == (2, b.c, spec.hidden)
+    same = oracle.autoregressive_draft(spec, w, b, 3, precision="mirror", forced_tokens=own["tokens"],
+                                       forced_hidden=own["fed_hidden"])
+    np.testing.assert_array_equal(same["logits"], own["logits"])
+    np.testing.assert_array_equal(same["fed_hidden"], own["fed_hidden"])
+    other = own["fed_hidden"].copy()
+    other[0] = np.float32(0.5) * other[0]
+    f = oracle.autoregressive_draft(spec, w, b, 3, precision="mirror", forced_tokens=own["tokens"],
+                                    forced_hidden=other)
+    np.testing.assert_array_equal(f["logits"][:, 0], own["logits"][:, 0])
+    assert np.max(np.abs(f["logits"][:, 1] - own["logits"][:, 1])) > 1e-6
