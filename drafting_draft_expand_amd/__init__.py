@@ -5,6 +5,7 @@ Public API (thin ctypes binding over libpeagle.so; all work runs in HIP):
 * :class:`DraftModel` -- drafter shape + borrowed device weights
 * :func:`prepare_draft_batch` -- expand the verified batch, place hidden states
 * :func:`draft_forward` -- one drafter pass producing K tokens per sequence
+* :func:`draft_forward_noalloc` -- the same pass on the library's static scratch (no workspace)
 * :func:`accept` -- greedy accepted length and next bonus token
 * :func:`draft_autoregressive` -- the K-pass autoregressive baseline on the same kernels
 * :func:`next_verified_batch` -- next round's verified batch from this round's results
@@ -18,6 +19,7 @@ from ._lib import (  # noqa: F401
     check_verified_batch,
     draft_autoregressive,
     draft_forward,
+    draft_forward_noalloc,
     load,
     next_verified_batch,
     prepare_draft_batch,

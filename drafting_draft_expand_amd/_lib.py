@@ -25,7 +25,9 @@ EXPORTED = ("pe_model_create", "pe_model_destroy", "pe_workspace_bytes", "pe_pre
             "pe_draft_forward", "pe_accept", "pe_status_string", "pe_timing_enable", "pe_timing_read",
             "pe_autoregressive_workspace_bytes", "pe_draft_autoregressive", "pe_next_verified_batch",
             "pe_prepare_draft_batch_compact", "pe_packed_weights_bytes", "pe_model_pack_weights",
-            "pe_check_verified_batch")
+            "pe_check_verified_batch", "pe_draft_forward_noalloc")
+
+STATIC_SCRATCH_BYTES = 32 << 20  # PE_STATIC_SCRATCH_BYTES
 
 
 class PeError(RuntimeError):
@@ -82,6 +84,8 @@ def load() -> ctypes.CDLL:
     lib.pe_prepare_draft_batch_compact.restype = I32
     lib.pe_draft_forward.argtypes = [P, I32, I32, I32] + [P] * 9 + [I32] + [P, P, P, SZ] + [P, P, P] + [P]
     lib.pe_draft_forward.restype = I32
+    lib.pe_draft_forward_noalloc.argtypes = [P, I32, I32, I32] + [P] * 9 + [I32] + [P, P] + [P, P, P] + [P]
+    lib.pe_draft_forward_noalloc.restype = I32
     lib.pe_accept.argtypes = [I32, I32, P, P, P, P, P]
     lib.pe_accept.restype = I32
     lib.pe_status_string.argtypes = [I32]
@@ -252,6 +256,25 @@ def draft_forward(model: DraftModel, batch: Dict[str, torch.Tensor], block_table
         ctypes.cast(kp, ctypes.c_void_p), ctypes.cast(vp, ctypes.c_void_p), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(tokens), _ptr(logits), _ptr(top2_gap), _stream(stream))
     _check(st, "pe_draft_forward")
+    return tokens
+
+
+def draft_forward_noalloc(model: DraftModel, batch: Dict[str, torch.Tensor], block_table: torch.Tensor,
+                          k_cache: Sequence[torch.Tensor], v_cache: Sequence[torch.Tensor],
+                          tokens: torch.Tensor, logits: Optional[torch.Tensor] = None,
+                          top2_gap: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One drafter pass on the library's static scratch (see pe_draft_forward_noalloc): no workspace,
+    nothing allocated here or in the library; the caller passes every output.  Returns ``tokens``."""
+    c, K, N = batch["num_seqs"], batch["K"], batch["num_rows"]
+    kp = (ctypes.c_void_p * len(k_cache))(*[_ptr(t) for t in k_cache])
+    vp = (ctypes.c_void_p * len(v_cache))(*[_ptr(t) for t in v_cache])
+    st = load().pe_draft_forward_noalloc(
+        model.handle, c, K, N, _ptr(batch["draft_ids"]), _ptr(batch["draft_pos"]), _ptr(batch["slot_mapping"]),
+        _ptr(batch["is_rejected"]), _ptr(batch["cu_draft"]), _ptr(batch["kv_lens"]), _ptr(batch["sample_idx"]),
+        _ptr(batch["draft_hidden"]), _ptr(block_table), int(block_table.shape[1]),
+        ctypes.cast(kp, ctypes.c_void_p), ctypes.cast(vp, ctypes.c_void_p), _ptr(tokens), _ptr(logits),
+        _ptr(top2_gap), _stream(stream))
+    _check(st, "pe_draft_forward_noalloc")
     return tokens
 
 

@@ -168,8 +168,8 @@ struct TimedScope {
   hipStream_t s;
   hipEvent_t stop = nullptr;
   std::unique_lock<std::mutex> lock;
-  TimedScope(pe_kernel_class k, hipStream_t stream) : t(&g_timing[k]), s(stream) {
-    if (!t->enabled.load(std::memory_order_relaxed)) { t = nullptr; return; }
+  TimedScope(pe_kernel_class k, hipStream_t stream, bool allowed = true) : t(&g_timing[k]), s(stream) {
+    if (!allowed || !t->enabled.load(std::memory_order_relaxed)) { t = nullptr; return; }
     lock = std::unique_lock<std::mutex>(g_timing_mu);
     if (!t->enabled.load(std::memory_order_relaxed)) { t = nullptr; return; }
     if (t->used == t->events.size()) {
@@ -395,14 +395,18 @@ pe_status pe_check_verified_batch(const pe_model* m, int32_t c, int32_t K, int32
   return PE_OK;
 }
 
-pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, const int32_t* draft_ids,
-                           const int32_t* draft_pos, const int64_t* slot_mapping,
-                           const uint8_t* is_rejected, const int32_t* cu_draft, const int32_t* kv_lens,
-                           const int32_t* sample_idx, const void* draft_hidden,
-                           const int32_t* block_table, int32_t max_blocks, void* const* k_cache,
-                           void* const* v_cache, void* workspace, size_t workspace_bytes,
-                           int32_t* draft_tokens, float* logits, float* top2_gap, hipStream_t stream) {
-  const pe_model* m = mc;  // read only: the handle is shared by every stream and thread
+}  // extern "C"
+
+namespace {
+// The drafter pass behind pe_draft_forward and pe_draft_forward_noalloc;
+// `timed`: launches may record kernel-timing events.
+pe_status forward_impl(const pe_model* m, int32_t c, int32_t K, int32_t N, const int32_t* draft_ids,
+                       const int32_t* draft_pos, const int64_t* slot_mapping, const uint8_t* is_rejected,
+                       const int32_t* cu_draft, const int32_t* kv_lens, const int32_t* sample_idx,
+                       const void* draft_hidden, const int32_t* block_table, int32_t max_blocks,
+                       void* const* k_cache, void* const* v_cache, void* workspace, size_t workspace_bytes,
+                       int32_t* draft_tokens, float* logits, float* top2_gap, hipStream_t stream, bool timed) {
+  // m is read only: the handle is shared by every stream and thread
   if (!m || c <= 0 || K <= 0 || N < c * K || max_blocks <= 0) return PE_EINVAL;
   if (m->d.n_layers <= 0) return PE_EUNSUPPORTED;
   const void* ptrs[] = {draft_ids, draft_pos, slot_mapping, is_rejected, cu_draft, kv_lens,
@@ -455,7 +459,7 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
     at.q = qrot; at.pos = draft_pos; at.rejected = is_rejected; at.cu_draft = cu_draft;
     at.kv_lens = kv_lens; at.block_table = block_table; at.k_cache = k_cache[l];
     at.v_cache = v_cache[l]; at.partial = part; at.out = act;
-    TimedScope ts(PE_KERNEL_ATTENTION, stream);
+    TimedScope ts(PE_KERNEL_ATTENTION, stream, timed);
     PE_HIP(pe::launch_attention(at, stream));
     return PE_OK;
   };
@@ -621,12 +625,80 @@ pe_status pe_draft_forward(const pe_model* mc, int32_t c, int32_t K, int32_t N, 
     g.logits = logits; g.partials = top2;
     if (pe::gemv_grid_x(S, d.vocab, pe::Epi::Argmax, t, cus, H) > ws.lm_parts) return PE_EUNSUPPORTED;
     {
-      TimedScope ts(PE_KERNEL_LM_HEAD, stream);
+      TimedScope ts(PE_KERNEL_LM_HEAD, stream, timed);
       if ((st = proj(g, pe::Epi::Argmax)) != PE_OK) return st;
     }
     PE_HIP(pe::launch_argmax_finalize(S, g.grid_x, top2, draft_tokens, top2_gap, stream));
   }
   return PE_OK;
+}
+
+// ------------------------------------------------------- allocation-free forward
+// The scratch of pe_draft_forward_noalloc: a file-scope device array, one per
+// GPU the library runs on, held until the process ends.  In host code its name
+// is a host-side stand-in, never a device address: host code uses only the
+// address hipGetSymbolAddress returns for the current device.  No part of the
+// drafter pass needs its workspace zeroed (every region is written before it
+// is read within a pass), so the array is used as the previous call left it.
+constexpr size_t kStaticScratch = PE_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratch];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the current device's array, looked up once per device.
+pe_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) {
+    (void)hipGetLastError();
+    return PE_EHIP;
+  }
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return PE_EHIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+pe_status pe_draft_forward(const pe_model* m, int32_t c, int32_t K, int32_t N, const int32_t* draft_ids,
+                           const int32_t* draft_pos, const int64_t* slot_mapping,
+                           const uint8_t* is_rejected, const int32_t* cu_draft, const int32_t* kv_lens,
+                           const int32_t* sample_idx, const void* draft_hidden,
+                           const int32_t* block_table, int32_t max_blocks, void* const* k_cache,
+                           void* const* v_cache, void* workspace, size_t workspace_bytes,
+                           int32_t* draft_tokens, float* logits, float* top2_gap, hipStream_t stream) {
+  return forward_impl(m, c, K, N, draft_ids, draft_pos, slot_mapping, is_rejected, cu_draft, kv_lens, sample_idx,
+                      draft_hidden, block_table, max_blocks, k_cache, v_cache, workspace, workspace_bytes,
+                      draft_tokens, logits, top2_gap, stream, true);
+}
+
+pe_status pe_draft_forward_noalloc(const pe_model* m, int32_t c, int32_t K, int32_t N, const int32_t* draft_ids,
+                                   const int32_t* draft_pos, const int64_t* slot_mapping,
+                                   const uint8_t* is_rejected, const int32_t* cu_draft, const int32_t* kv_lens,
+                                   const int32_t* sample_idx, const void* draft_hidden,
+                                   const int32_t* block_table, int32_t max_blocks, void* const* k_cache,
+                                   void* const* v_cache, int32_t* draft_tokens, float* logits, float* top2_gap,
+                                   hipStream_t stream) {
+  // the size limit is checked before any HIP call
+  if (!m || c <= 0 || K <= 0 || N < c * K || m->d.n_layers <= 0) return m && m->d.n_layers <= 0 ? PE_EUNSUPPORTED
+                                                                                               : PE_EINVAL;
+  if (plan_workspace(m, c, K, N).total > kStaticScratch) return PE_EWORKSPACE;
+  void* ws = nullptr;
+  const pe_status st = scratch_of_current_device(&ws);
+  if (st != PE_OK) return st;
+  return forward_impl(m, c, K, N, draft_ids, draft_pos, slot_mapping, is_rejected, cu_draft, kv_lens, sample_idx,
+                      draft_hidden, block_table, max_blocks, k_cache, v_cache, ws, kStaticScratch, draft_tokens,
+                      logits, top2_gap, stream, false);
 }
 
 // ---------------------------------------------------------------- autoregressive baseline

@@ -244,6 +244,35 @@ pe_status pe_draft_forward(const pe_model *model, int32_t num_seqs, int32_t K, i
                            size_t workspace_bytes, int32_t *draft_tokens, float *logits_or_null,
                            float *top2_gap_or_null, hipStream_t stream);
 
+/* Allocation-free variant of pe_draft_forward, for callers that cannot
+ * allocate device memory or carry a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments
+ * (minus the workspace), kernels and results as pe_draft_forward.  Its scratch
+ * is a static device array of PE_STATIC_SCRATCH_BYTES inside the library, one
+ * per GPU it runs on, held until the process ends; the call itself never
+ * allocates or frees memory.
+ *   - Returns PE_EWORKSPACE before anything is enqueued when the batch needs
+ *     more scratch than that (pe_workspace_bytes(model, c, K, N) >
+ *     PE_STATIC_SCRATCH_BYTES; 32 MiB covers, e.g., one sequence of a
+ *     GPT-OSS-20B-shaped drafter at K <= 8, or 16 sequences of a
+ *     Qwen3-Coder-30B-shaped one at K = 3), PE_EHIP when the array's device
+ *     address cannot be obtained; otherwise as pe_draft_forward.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents (the pass writes every scratch region it reads first).
+ *     Calls that overlap in time on one GPU -- on different streams, or from
+ *     host threads without ordering between them -- race on the array and
+ *     corrupt each other's results: serialize them.
+ *   - Its launches are not recorded by the kernel timing (pe_timing_*). */
+#define PE_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+pe_status pe_draft_forward_noalloc(const pe_model *model, int32_t num_seqs, int32_t K, int32_t num_rows,
+                                   const int32_t *draft_ids, const int32_t *draft_pos,
+                                   const int64_t *slot_mapping, const uint8_t *is_rejected,
+                                   const int32_t *cu_draft, const int32_t *kv_lens,
+                                   const int32_t *sample_idx, const void *draft_hidden,
+                                   const int32_t *block_table, int32_t max_blocks,
+                                   void *const *k_cache, void *const *v_cache, int32_t *draft_tokens,
+                                   float *logits_or_null, float *top2_gap_or_null, hipStream_t stream);
+
 /* Greedy acceptance ([PP] Acceptance Length (AL)): num_accepted[i] = length of
  * the longest prefix on which draft_tokens[i*K..] equals target_tokens[i*(K+1)..],
  * bonus_ids[i] = target_tokens[i*(K+1) + num_accepted[i]].

@@ -171,3 +171,27 @@ def test_timing_api_without_launches(lib):
     ms, n = ctypes.c_double(), ctypes.c_int64()
     assert lib.pe_timing_read(7, ctypes.byref(ms), ctypes.byref(n), None, 0) == -1
     assert lib.pe_timing_enable(-1, 1) == -1
+
+
+def test_noalloc_forward_rejects_batches_beyond_its_scratch(lib):
+    """pe_draft_forward_noalloc refuses, before any HIP call, a batch whose
+    scratch would exceed the static array (GPT-OSS-20B shape, 64 sequences at
+    K = 7: about 200 MiB against 32 MiB)."""
+    from drafting_draft_expand_amd import _lib
+    d = _desc(hidden=2880, vocab=201088, n_q=64, n_kv=8, head_dim=64, inter=7680, mask_token_id=201087, dtype=1)
+    st, h = _create(lib, d)
+    assert st == 0
+    try:
+        P = 0x20000
+        kp = (ctypes.c_void_p * 1)(P)
+        c, K, N = 64, 7, 896
+        assert lib.pe_workspace_bytes(h, c, K, N) > _lib.STATIC_SCRATCH_BYTES
+        args = [h, c, K, N] + [P] * 9 + [600, ctypes.cast(kp, ctypes.c_void_p), ctypes.cast(kp, ctypes.c_void_p),
+                                         P, None, None, None]
+        assert lib.pe_draft_forward_noalloc(*args) == -3
+        bad = list(args)
+        bad[3] = 100  # fewer rows than c * K
+        assert lib.pe_draft_forward_noalloc(*bad) == -1
+        assert lib.pe_workspace_bytes(h, 1, 7, 14) <= _lib.STATIC_SCRATCH_BYTES
+    finally:
+        lib.pe_model_destroy(h)
