@@ -453,6 +453,96 @@ def _traffic(name):
 C64_WORKLOAD = "gptoss20b-bf16-c64-k7"
 
 
+def _short_kernel(n: str) -> str:
+    import re
+    n = re.sub(r"\(pe::GemvArgs.*|\(pe::AttnArgs.*|\(pe::PrepareArgs.*|\(int,.*|\(pe::Top2.*|\(pe::PackArgs.*", "", n)
+    n = n.replace("void ", "").replace("pe::(anonymous namespace)::", "").replace("(pe::Epi)", "E")
+    return n.replace("(pe::AMode)", "A").replace("unsigned short", "bf16")[:72]
+
+
+def _summarize_trace(paths) -> int:
+    """Markdown table of a rocprofv3 kernel trace (run_kernel_trace.csv): the
+    rounds (each starts at the expansion kernel), grouped by kernel sequence,
+    with the median duration of the kernel at each position."""
+    import csv
+    from collections import defaultdict
+    for path in paths:
+        rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+        rounds, cur = [], None
+        for r in rows:
+            if "prepare_kernel" in r["Kernel_Name"]:
+                cur = []
+                rounds.append(cur)
+            if cur is not None:
+                threads = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+                wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
+                cur.append((_short_kernel(r["Kernel_Name"]), threads, wg, int(r["Start_Timestamp"]),
+                            int(r["End_Timestamp"])))
+        groups = defaultdict(list)
+        for rd in rounds:
+            groups[tuple((k[0], k[1]) for k in rd)].append(rd)
+        print(f"Trace `{path}`\n")
+        for sig, rds in sorted(groups.items(), key=lambda kv: -len(kv[1])):
+            if len(rds) < 3:
+                continue
+            span = statistics.median([(rd[-1][4] - rd[0][3]) / 1e3 for rd in rds])
+            print(f"{len(rds)} rounds of {len(sig)} kernels; median round span {span:.1f} us (first start to "
+                  f"last end)\n")
+            print("| # | kernel | workgroups x threads | median us | % of round |")
+            print("|---:|---|---:|---:|---:|")
+            for i, (name, grid) in enumerate(sig):
+                d = statistics.median([(rd[i][4] - rd[i][3]) / 1e3 for rd in rds])
+                print(f"| {i} | `{name}` | {grid // rds[0][i][2]} x {rds[0][i][2]} | {d:.2f} | {100 * d / span:.1f} |")
+            print()
+    return 0
+
+
+def _summarize_counters(paths) -> int:
+    """Markdown table of rocprofv3 --pmc runs (run_counter_collection.csv): per
+    kernel (name and grid), the median value per dispatch of every counter,
+    with MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD * SIMDs)
+    (GRBM_GUI_ACTIVE comes summed over the XCDs, each of which counts the
+    kernel's cycles) and MFMA FLOPs = SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 where
+    those were counted."""
+    import csv
+    from collections import defaultdict
+    vals = defaultdict(lambda: defaultdict(list))
+    simds, xcc = None, 1
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            key = (_short_kernel(r["Kernel_Name"]), r.get("Grid_Size", ""))
+            vals[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    for path in paths:
+        info = os.path.join(os.path.dirname(path), os.path.basename(path).replace("counter_collection", "agent_info"))
+        if os.path.exists(info):
+            for r in csv.DictReader(open(info)):
+                if r.get("Agent_Type", "").endswith("GPU") and r.get("Simd_Count"):
+                    simds = int(r["Simd_Count"])
+                    xcc = int(r.get("Num_Xcc") or 1)
+    names = sorted({c for v in vals.values() for c in v})
+    head = ["kernel", "grid"] + names
+    derived = []
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in names and "GRBM_GUI_ACTIVE" in names and simds:
+        derived.append("MfmaUtil %")
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in names:
+        derived.append("MFMA GFLOP")
+    print("| " + " | ".join(head + derived) + " |")
+    print("|" + "---|" * 2 + "---:|" * (len(names) + len(derived)))
+    for (k, grid), cv in sorted(vals.items(), key=lambda kv: -max((sum(v) for v in kv[1].values()), default=0)):
+        med = {c: statistics.median(v) for c, v in cv.items()}
+        cells = [f"`{k}`", grid] + [f"{med[c]:.6g}" if c in med else "" for c in names]
+        if "MfmaUtil %" in derived:
+            busy, act = med.get("SQ_VALU_MFMA_BUSY_CYCLES"), med.get("GRBM_GUI_ACTIVE")
+            cells.append(f"{100.0 * busy / (act / xcc * simds):.1f}" if busy is not None and act else "")
+        if "MFMA GFLOP" in derived:
+            mops = med.get("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+            cells.append(f"{mops * 512 / 1e9:.2f}" if mops is not None else "")
+        print("| " + " | ".join(cells) + " |")
+    if simds:
+        print(f"\nSIMDs: {simds}; XCDs: {xcc} (GRBM_GUI_ACTIVE above is the sum over the XCDs)")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -477,7 +567,15 @@ def main() -> int:
                     help="draft layout: fixed (rejected rows kept as inert rows) or compact (dropped)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy five times (reference for the HBM byte counters)")
+    ap.add_argument("--summarize-trace", nargs="+", metavar="CSV",
+                    help="print per-position kernel times of rocprofv3 kernel traces and exit (no GPU)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                    help="print per-kernel medians of rocprofv3 --pmc counter files and exit (no GPU)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        return _summarize_trace(args.summarize_trace)
+    if args.summarize_counters:
+        return _summarize_counters(args.summarize_counters)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
                           "n_gpus_requested": args.gpus}))

@@ -187,6 +187,11 @@ def _workloads() -> dict:
         "gptoss20b-bf16-c64-k7", GPTOSS20B, c=64, K=7, ctx_lo=512, ctx_hi=8192, accept_hi=7,
         seed=3, weight_seed=2,
         description="GPT-OSS-20B-shaped drafter, c=64, K=7, contexts U{512..8192} paged")
+    w["gptoss20b-bf16-c64-k8"] = Workload(
+        "gptoss20b-bf16-c64-k8", GPTOSS20B, c=64, K=8, ctx_lo=512, ctx_hi=8192, accept_hi=8,
+        seed=3, weight_seed=2,
+        description="GPT-OSS-20B-shaped drafter, c=64, K=8: 512 sampled rows into the LM head "
+                    "(the 512-row LM-head figure beside the 448 rows of K=7)")
     for k in (3, 5, 7):
         name = f"qwen3coder30b-bf16-c16-k{k}"
         w[name] = Workload(
