@@ -195,26 +195,25 @@ __device__ __forceinline__ void rope_cos_sin(int pos, double inv_freq, float& c,
 }
 
 // Best and runner-up logit of a set of vocabulary rows (ties -> lowest id).
+// (both sides evaluated: a short-circuit here becomes a branch per compare)
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
+  return (va > vb) | ((va == vb) & (ia < ib));
 }
 __device__ __forceinline__ void top2_push(Top2& t, float v, int i) {
-  if (better(v, i, t.v1, t.i1)) {
-    t.v2 = t.v1;
-    t.v1 = v;
-    t.i1 = i;
-  } else if (v > t.v2) {
-    t.v2 = v;
-  }
+  const bool b = better(v, i, t.v1, t.i1);
+  t.v2 = b ? t.v1 : (v > t.v2 ? v : t.v2);
+  t.v1 = b ? v : t.v1;
+  t.i1 = b ? i : t.i1;
 }
+// (selects rather than a swap, so that no lane takes a branch)
 __device__ __forceinline__ Top2 top2_merge(Top2 a, Top2 b) {
-  if (better(b.v1, b.i1, a.v1, a.i1)) {
-    Top2 t = a;
-    a = b;
-    b = t;
-  }
-  a.v2 = fmaxf(a.v2, b.v1);
-  return a;
+  const bool s = better(b.v1, b.i1, a.v1, a.i1);
+  Top2 r;
+  r.v1 = s ? b.v1 : a.v1;
+  r.i1 = s ? b.i1 : a.i1;
+  r.v2 = fmaxf(s ? b.v2 : a.v2, s ? a.v1 : b.v1);
+  r.pad = s ? b.pad : a.pad;
+  return r;
 }
 __device__ __forceinline__ Top2 top2_empty() {
   Top2 t;

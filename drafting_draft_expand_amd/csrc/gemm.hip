@@ -193,32 +193,68 @@ __device__ __forceinline__ void tile_epilogue(const GemvArgs& a, f32x4 (&acc)[TM
         }
       }
   } else {  // Argmax over this tile's BN columns, per row
+    if (a.logits) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int jn = 0; jn < TN; ++jn) {
+          const int n = nt * BN + wn * WN + jn * 16 + l16;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int m = m0 + wm * WM + i * 16 + lq * 4 + q;
+            if (m < a.M && n < a.Nout) a.logits[static_cast<int64_t>(m) * a.Nout + n] = acc[i][jn][q];
+          }
+        }
+    }
+    // Each lane's TM * 4 rows: the candidates of its TN columns merged
+    // pairwise (a column past Nout adds nothing) ...
+    static_assert(TM == 4 && (TN & (TN - 1)) == 0, "16 rows per lane, a power-of-two column count");
+    Top2 t[16];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int m = m0 + wm * WM + i * 16 + lq * 4 + q;
-        Top2 t = top2_empty();
+        Top2 c[TN];
 #pragma unroll
         for (int jn = 0; jn < TN; ++jn) {
           const int n = nt * BN + wn * WN + jn * 16 + l16;
-          if (n < a.Nout) {
-            const float v = acc[i][jn][q];
-            if (a.logits && m < a.M) a.logits[static_cast<int64_t>(m) * a.Nout + n] = v;
-            top2_push(t, v, n);
-          }
+          // one column as a candidate set: itself, or nothing if it lies
+          // past Nout or is NaN (what pushing it into an empty set gives)
+          const float v = acc[i][jn][q];
+          const bool ok = n < a.Nout && v == v;
+          c[jn] = top2_empty();
+          c[jn].v1 = ok ? v : c[jn].v1;
+          c[jn].i1 = ok ? n : c[jn].i1;
         }
 #pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) {
-          Top2 o;
-          o.v1 = __shfl_xor(t.v1, off, 64);
-          o.i1 = __shfl_xor(t.i1, off, 64);
-          o.v2 = __shfl_xor(t.v2, off, 64);
-          o.pad = 0;
-          t = top2_merge(t, o);
-        }
-        if (l16 == 0) red[wn * BM + wm * WM + i * 16 + lq * 4 + q] = t;
+        for (int w = 1; w < TN; w *= 2)
+#pragma unroll
+          for (int jn = 0; jn < TN; jn += 2 * w) c[jn] = top2_merge(c[jn], c[jn + w]);
+        t[i * 4 + q] = c[0];
       }
+    // ... then exchanged over the 16 lanes that hold the same rows: at
+    // distance o a lane keeps the half of its o * 2 rows that bit o of its
+    // lane index selects and merges in its partner's candidates for that
+    // half, so after four steps lane l16 holds row l16 (i = l16 / 4,
+    // q = l16 % 4) merged over all 16 lanes.  The merge result does not
+    // depend on the order (best value, lowest id on ties; runner-up = largest
+    // of the rest), so this equals the row-by-row reduction.
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) {
+      const bool up = (l16 & o) != 0;
+#pragma unroll
+      for (int r = 0; r < o; ++r) {
+        const Top2 keep = up ? t[r + o] : t[r];
+        const Top2 give = up ? t[r] : t[r + o];
+        Top2 got;
+        got.v1 = __shfl_xor(give.v1, o, 64);
+        got.i1 = __shfl_xor(give.i1, o, 64);
+        got.v2 = __shfl_xor(give.v2, o, 64);
+        got.pad = 0;
+        t[r] = top2_merge(keep, got);
+      }
+    }
+    red[wn * BM + wm * WM + (l16 >> 2) * 16 + lq * 4 + (l16 & 3)] = t[0];
     __syncthreads();
     for (int r = tid; r < BM; r += NT) {
       const int m = m0 + r;
@@ -555,32 +591,45 @@ __global__ __launch_bounds__(256, ST * (BM + BN) * 64 > 80 * 1024 ? 1 : 2) void 
   using C0 = std::integral_constant<int, 0>;
 
   if constexpr (PF) {
-    // prologue: steps 0 .. ST-1 requested, stages 0 and 1 landed everywhere,
-    // step 0's fragments in registers and every wave done reading slot 0
-    static_for<ST>([&](auto s_c) { request(decltype(s_c)::value, s_c); });
-    sync();
-    frags(C0{}, C0{});
-    sync();
-    auto step = [&](int t, auto j_c) __attribute__((always_inline)) {
-      constexpr int J = decltype(j_c)::value;
-      request(t + ST, std::integral_constant<int, J % ST>{});
-      __builtin_amdgcn_sched_barrier(0);
-      frags(std::integral_constant<int, (J + 1) % ST>{}, std::integral_constant<int, (J + 1) & 1>{});
-      mma(std::integral_constant<int, J & 1>{});
-      // one fragment read, then two MFMAs, ..., then the remaining MFMAs
-      static_for<TM + TN>([&](auto) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      });
-      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - 2 * (TM + TN), 0);
+    // A wave whose rows all lie past M (the last M tile of a row count that
+    // is not a multiple of BM) still issues its share of the copies and meets
+    // every barrier, but reads no fragments and runs no MFMAs: its SIMD goes
+    // to the other workgroup on the CU.  Its accumulators stay zero, and the
+    // epilogue writes no row past M.
+    auto run = [&](auto live_c) __attribute__((always_inline)) {
+      constexpr bool LIVE = decltype(live_c)::value;
+      // prologue: steps 0 .. ST-1 requested, stages 0 and 1 landed
+      // everywhere, step 0's fragments in registers and every wave done
+      // reading slot 0
+      static_for<ST>([&](auto s_c) { request(decltype(s_c)::value, s_c); });
       sync();
+      if constexpr (LIVE) frags(C0{}, C0{});
+      sync();
+      auto step = [&](int t, auto j_c) __attribute__((always_inline)) {
+        constexpr int J = decltype(j_c)::value;
+        request(t + ST, std::integral_constant<int, J % ST>{});
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (LIVE) {
+          frags(std::integral_constant<int, (J + 1) % ST>{}, std::integral_constant<int, (J + 1) & 1>{});
+          mma(std::integral_constant<int, J & 1>{});
+          // one fragment read, then two MFMAs, ..., then the remaining MFMAs
+          static_for<TM + TN>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          });
+          __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - 2 * (TM + TN), 0);
+        }
+        sync();
+      };
+      constexpr int U = ST % 2 == 0 ? ST : 2 * ST;
+      int t = 0;
+      for (; t + U <= nk; t += U) static_for<U>([&](auto j_c) { step(t + decltype(j_c)::value, j_c); });
+      static_for<U - 1>([&](auto j_c) {
+        if (t + decltype(j_c)::value < nk) step(t + decltype(j_c)::value, j_c);
+      });
     };
-    constexpr int U = ST % 2 == 0 ? ST : 2 * ST;
-    int t = 0;
-    for (; t + U <= nk; t += U) static_for<U>([&](auto j_c) { step(t + decltype(j_c)::value, j_c); });
-    static_for<U - 1>([&](auto j_c) {
-      if (t + decltype(j_c)::value < nk) step(t + decltype(j_c)::value, j_c);
-    });
+    if (m0 + wm * WM < a.M) run(std::true_type{});
+    else run(std::false_type{});
   } else {
     static_for<ST - 1>([&](auto s_c) { request(decltype(s_c)::value, s_c); });
     auto step = [&](int t, auto s_c) __attribute__((always_inline)) {
