@@ -462,18 +462,22 @@ __global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel
 // Row group of the tile-major W copy (packed_tile_bytes / launch_pack_tiles).
 constexpr int kTileGroup = 256;
 
-template <int BM, int BN, int ST, bool PF, bool PKA, bool PKW, Epi EPI>
-__global__ __launch_bounds__(256, ST * (BM + BN) * 64 > 80 * 1024 ? 1 : 2) void gemm_ring_kernel(GemvArgs a,
-                                                                                              int num_m, int num_n,
-                                                                                              int splits) {
-  constexpr int BK = 32, CPR = 4, WGM = 2, WGN = 2;
+template <int BM, int BN, int ST, bool PF, bool PKA, bool PKW, Epi EPI, int BKS = 32>
+__global__ __launch_bounds__(256, ST * (BM + BN) * BKS * 2 > 80 * 1024 ? 1 : 2) void gemm_ring_kernel(GemvArgs a,
+                                                                                                   int num_m, int num_n,
+                                                                                                   int splits) {
+  // BKS: K depth of one stage.  32: a copy instruction moves 16 tile rows of
+  // 64 bytes; 64: 8 rows of 128 bytes (whole cache lines of row-major
+  // operands, two MFMA K steps per stage; row-major operands, no prefetch).
+  constexpr int BK = BKS, CPR = BK / 8, KK = BK / 32, RPC = 512 / BK, WGM = 2, WGN = 2;
+  static_assert(BK == 32 || (BK == 64 && !PF && !PKA && !PKW), "64-deep stages: row-major operands, no prefetch");
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 16, TN = WN / 16;
   static_assert(!PKW || EPI == Epi::Argmax || EPI == Epi::Store || EPI == Epi::AddTo,
                 "the tile-major copy holds W rows in plain order");
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "whole 16-row copy blocks for every wave");
+  static_assert(BM % (4 * RPC) == 0 && BN % (4 * RPC) == 0, "whole copy blocks for every wave");
   static_assert(!PKW || kTileGroup % BN == 0, "a W tile lies inside one packed row group");
-  constexpr int IA = BM / 64, IB = BN / 64;  // copy instructions per wave and stage
+  constexpr int IA = BM / (4 * RPC), IB = BN / (4 * RPC);  // copy instructions per wave and stage
   constexpr int NI = IA + IB;
   static_assert(ST >= 3 && (ST - 2) * NI <= 63, "outstanding copy count must fit the counter");
   static_assert(WGN * BM * sizeof(Top2) <= sizeof(bf16_t) * (BM + BN) * BK, "argmax scratch must fit one ring stage");
@@ -512,12 +516,14 @@ __global__ __launch_bounds__(256, ST * (BM + BN) * 64 > 80 * 1024 ? 1 : 2) void 
 
   // this lane's source chunk in each of the wave's copy blocks, at K step 0,
   // and the element stride from one K step to the next
-  const int lrow = lane >> 2;
+  const int lrow = lane / CPR;
+  // global chunk that the row's swizzle (lds_off) places in this lane's slot
+  auto chunk_of = [&](int r) { return CPR == 8 ? (lane & 7) ^ (r & 7) : (lane & 3) ^ ((r >> 1) & 3); };
   const bf16_t* ap[IA];
 #pragma unroll
   for (int q = 0; q < IA; ++q) {
-    const int r = (q * 4 + wave) * 16 + lrow;
-    const int gc = (lane & 3) ^ ((r >> 1) & 3);
+    const int r = (q * 4 + wave) * RPC + lrow;
+    const int gc = chunk_of(r);
     if constexpr (PKA)
       ap[q] = static_cast<const bf16_t*>(a.x) + (static_cast<int64_t>(mt) * nk_all * BM + r) * BK + gc * 8;
     else
@@ -526,8 +532,8 @@ __global__ __launch_bounds__(256, ST * (BM + BN) * 64 > 80 * 1024 ? 1 : 2) void 
   const bf16_t* bp[IB];
 #pragma unroll
   for (int q = 0; q < IB; ++q) {
-    const int r = (q * 4 + wave) * 16 + lrow;
-    const int gc = (lane & 3) ^ ((r >> 1) & 3);
+    const int r = (q * 4 + wave) * RPC + lrow;
+    const int gc = chunk_of(r);
     if constexpr (PKW) {
       const int row = nt * BN + r;  // rows past Nout exist in the packed copy
       bp[q] = static_cast<const bf16_t*>(a.pk_tiles) +
@@ -547,9 +553,9 @@ __global__ __launch_bounds__(256, ST * (BM + BN) * 64 > 80 * 1024 ? 1 : 2) void 
     bf16_t* st = ring(s_c);
     const int64_t k = kbase + min(kt, nk - 1);
 #pragma unroll
-    for (int q = 0; q < IA; ++q) dma16(ap[q] + k * A_STEP, st + (q * 4 + wave) * 16 * BK);
+    for (int q = 0; q < IA; ++q) dma16(ap[q] + k * A_STEP, st + (q * 4 + wave) * RPC * BK);
 #pragma unroll
-    for (int q = 0; q < IB; ++q) dma16<W_STREAM>(bp[q] + k * B_STEP, st + BM * BK + (q * 4 + wave) * 16 * BK);
+    for (int q = 0; q < IB; ++q) dma16<W_STREAM>(bp[q] + k * B_STEP, st + BM * BK + (q * 4 + wave) * RPC * BK);
   };
 
   f32x4 acc[TM][TN];
@@ -559,26 +565,32 @@ __global__ __launch_bounds__(256, ST * (BM + BN) * 64 > 80 * 1024 ? 1 : 2) void 
     for (int jn = 0; jn < TN; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int l16 = lane & 15, lq = lane >> 4;
   constexpr int NF = PF ? 2 : 1;  // fragment sets
-  u32x4 fa[NF][TM], fb[NF][TN];
+  u32x4 fa[NF][KK][TM], fb[NF][KK][TN];
   auto frags = [&](auto s_c, auto f_c) __attribute__((always_inline)) {
     constexpr int F = decltype(f_c)::value;
     const bf16_t* as = ring(s_c);
     const bf16_t* bs = as + BM * BK;
 #pragma unroll
-    for (int jn = 0; jn < TN; ++jn)
-      fb[F][jn] = *reinterpret_cast<const u32x4*>(&bs[lds_off<CPR>(wn * WN + jn * 16 + l16, lq)]);
+    for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-      fa[F][i] = *reinterpret_cast<const u32x4*>(&as[lds_off<CPR>(wm * WM + i * 16 + l16, lq)]);
+      for (int jn = 0; jn < TN; ++jn)
+        fb[F][kk][jn] = *reinterpret_cast<const u32x4*>(&bs[lds_off<CPR>(wn * WN + jn * 16 + l16, kk * 4 + lq)]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        fa[F][kk][i] = *reinterpret_cast<const u32x4*>(&as[lds_off<CPR>(wm * WM + i * 16 + l16, kk * 4 + lq)]);
+    }
   };
   auto mma = [&](auto f_c) __attribute__((always_inline)) {
     constexpr int F = decltype(f_c)::value;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-      for (int jn = 0; jn < TN; ++jn)
-        acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[F][i]),
-                                                             __builtin_bit_cast(bf16x8, fb[F][jn]), acc[i][jn], 0, 0, 0);
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int jn = 0; jn < TN; ++jn)
+          acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[F][kk][i]),
+                                                               __builtin_bit_cast(bf16x8, fb[F][kk][jn]), acc[i][jn], 0, 0,
+                                                               0);
   };
   // wait until at most ST-2 stages of copies are in flight and no LDS read
   // is, then meet the other waves
@@ -655,18 +667,19 @@ __global__ __launch_bounds__(256, ST * (BM + BN) * 64 > 80 * 1024 ? 1 : 2) void 
 
 int gemm_splits(const GemvArgs& a, Epi epi, int tiles, int nk_all, int num_cus);
 
-template <int BM, int BN, int ST, bool PF, bool PKA, bool PKW, Epi EPI>
+template <int BM, int BN, int ST, bool PF, bool PKA, bool PKW, Epi EPI, int BKS = 32>
 hipError_t launch_ring(GemvArgs& a, int num_cus, hipStream_t s) {
   const int num_m = (a.M + BM - 1) / BM;
   const int cols = EPI == Epi::SiluMul ? BN / 2 : BN;  // gate + up rows per output column
   const int num_n = (a.Nout + cols - 1) / cols;
-  const int splits = gemm_splits(a, EPI, num_m * num_n, a.K / 32, num_cus);
+  if (a.K % BKS != 0) return hipErrorInvalidValue;
+  const int splits = gemm_splits(a, EPI, num_m * num_n, a.K / BKS, num_cus);
   const int total = num_m * num_n * splits;
   const int grid = ((total + 7) / 8) * 8;
   a.grid_x = num_n;
   a.splits = splits;
-  hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, ST, PF, PKA, PKW, EPI>), dim3(grid), dim3(256), 0, s, a, num_m, num_n,
-                     splits);
+  hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, ST, PF, PKA, PKW, EPI, BKS>), dim3(grid), dim3(256), 0, s, a, num_m,
+                     num_n, splits);
   return hipGetLastError();
 }
 
@@ -724,6 +737,22 @@ hipError_t launch_t(GemvArgs& a, int num_cus, hipStream_t s) {
   return hipGetLastError();
 }
 
+// 17..256 rows: the LDS-DMA ring on 64 x 64 tiles with five 64-deep stages
+// (each copy moves 8 rows of 128 bytes, whole cache lines of the row-major
+// operands; 80 KiB of LDS, two workgroups per CU), K split as gemm_splits
+// decides for Store / AddTo into partials.  A stage is waited for as a whole
+// and nearly every stage holds some line that misses L2, so a workgroup moves
+// about (stages - 2) x 16 KiB per memory round trip; two workgroups per CU
+// with five stages keep the most bytes in flight.  Qwen-shaped layer at
+// c = 16 (cold weights): steps 302 / 311 / 338 -> 287 / 301 / 332 us at
+// K = 3 / 5 / 7 against the register-staged 128-row tiles; wider tiles
+// (96 to 256 columns, one workgroup per CU, more K splits) and six stages
+// ran slower.
+template <Epi EPI>
+hipError_t launch_mid(GemvArgs& a, int num_cus, hipStream_t s) {
+  return launch_ring<64, 64, 5, false, false, false, EPI, 64>(a, num_cus, s);
+}
+
 template <Epi EPI, AMode MODE>
 hipError_t launch_cfg(GemvArgs& a, int num_cus, hipStream_t s) {
   // Many rows (more than two 128-row tiles) on a plain operand: the LDS-DMA
@@ -740,6 +769,11 @@ hipError_t launch_cfg(GemvArgs& a, int num_cus, hipStream_t s) {
       else if (a.part)
         return launch_ring<128, 256, 3, false, false, false, EPI>(a, num_cus, s);
     }
+  }
+  if constexpr (MODE == AMode::Plain && EPI != Epi::Argmax) {
+    if (a.M > 16 && a.M <= 256 && !a.ss_out && a.K % 64 == 0 &&
+        (EPI == Epi::QkvRope || EPI == Epi::SiluMul || a.part))
+      return launch_mid<EPI>(a, num_cus, s);
   }
   TileCfg t = pick_tile(a.M, a.Nout, EPI, num_cus);
   // Store / AddTo into split partials: 128 x 128 tiles, K split to fill the CUs

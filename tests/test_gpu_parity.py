@@ -219,9 +219,10 @@ def test_forward_bf16_many_sampled_rows(pack):
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_forward_bf16_mid_rows(d):
-    """200 draft rows (two 128-row tiles, the second ragged): the register-staged
-    tiled GEMM with narrow tiles, 128 x 64 for q/k/v with RoPE and gate/up, and
-    K split into partials for the residual projections."""
+    """200 draft rows (four 64-row tiles, the last ragged): the LDS-DMA ring
+    with 64-deep stages on 64 x 64 tiles for q/k/v with RoPE and gate/up, and
+    K split into partials for the residual projections; the fc input is
+    gathered by the register-staged tiled GEMM."""
     spec = synth.ModelSpec(hidden=256, vocab=900, n_layers=1, n_q=4, n_kv=2, head_dim=d, inter=320)
     wl = synth.Workload(f"mid-rows-d{d}", spec, c=20, K=5, ctx_lo=10, ctx_hi=200, accept_hi=5, seed=95 + d)
     _forward_case(wl)
