@@ -462,7 +462,7 @@ __global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel
 // Row group of the tile-major W copy (packed_tile_bytes / launch_pack_tiles).
 constexpr int kTileGroup = 256;
 
-template <int BM, int BN, int ST, bool PF, bool PKA, bool PKW, Epi EPI, int BKS = 32>
+template <int BM, int BN, int ST, bool PF, bool PKA, bool PKW, Epi EPI, int BKS = 32, bool GA = false>
 __global__ __launch_bounds__(256, ST * (BM + BN) * BKS * 2 > 80 * 1024 ? 1 : 2) void gemm_ring_kernel(GemvArgs a,
                                                                                                    int num_m, int num_n,
                                                                                                    int splits) {
@@ -471,6 +471,9 @@ __global__ __launch_bounds__(256, ST * (BM + BN) * BKS * 2 > 80 * 1024 ? 1 : 2) 
   // operands, two MFMA K steps per stage; row-major operands, no prefetch).
   constexpr int BK = BKS, CPR = BK / 8, KK = BK / 32, RPC = 512 / BK, WGM = 2, WGN = 2;
   static_assert(BK == 32 || (BK == 64 && !PF && !PKA && !PKW), "64-deep stages: row-major operands, no prefetch");
+  // GA: the A rows are gathered, [embed[ids[m]] ; x2[m]] (K / 2 elements
+  // each, K / 2 a multiple of the stage depth), as the fc input
+  static_assert(!GA || (!PKA && !PF), "gathered A rows are row-major");
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 16, TN = WN / 16;
   static_assert(!PKW || EPI == Epi::Argmax || EPI == Epi::Store || EPI == Epi::AddTo,
@@ -520,11 +523,16 @@ __global__ __launch_bounds__(256, ST * (BM + BN) * BKS * 2 > 80 * 1024 ? 1 : 2) 
   // global chunk that the row's swizzle (lds_off) places in this lane's slot
   auto chunk_of = [&](int r) { return CPR == 8 ? (lane & 7) ^ (r & 7) : (lane & 3) ^ ((r >> 1) & 3); };
   const bf16_t* ap[IA];
+  const bf16_t* ap_hi[GA ? IA : 1];  // GA: the second half's rows, offset by -K / 2
 #pragma unroll
   for (int q = 0; q < IA; ++q) {
     const int r = (q * 4 + wave) * RPC + lrow;
     const int gc = chunk_of(r);
-    if constexpr (PKA)
+    if constexpr (GA) {
+      const int m = min(m0 + r, a.M - 1), half = a.K / 2;
+      ap[q] = static_cast<const bf16_t*>(a.embed) + static_cast<int64_t>(a.ids[m]) * half + gc * 8;
+      ap_hi[q] = static_cast<const bf16_t*>(a.x2) + static_cast<int64_t>(m) * half + gc * 8 - half;
+    } else if constexpr (PKA)
       ap[q] = static_cast<const bf16_t*>(a.x) + (static_cast<int64_t>(mt) * nk_all * BM + r) * BK + gc * 8;
     else
       ap[q] = static_cast<const bf16_t*>(a.x) + static_cast<int64_t>(min(m0 + r, a.M - 1)) * a.K + gc * 8;
@@ -553,7 +561,11 @@ __global__ __launch_bounds__(256, ST * (BM + BN) * BKS * 2 > 80 * 1024 ? 1 : 2) 
     bf16_t* st = ring(s_c);
     const int64_t k = kbase + min(kt, nk - 1);
 #pragma unroll
-    for (int q = 0; q < IA; ++q) dma16(ap[q] + k * A_STEP, st + (q * 4 + wave) * RPC * BK);
+    for (int q = 0; q < IA; ++q) {
+      const bf16_t* src = ap[q];
+      if constexpr (GA) src = k * BK < a.K / 2 ? ap[q] : ap_hi[q];  // the same half for the whole stage
+      dma16(src + k * A_STEP, st + (q * 4 + wave) * RPC * BK);
+    }
 #pragma unroll
     for (int q = 0; q < IB; ++q) dma16<W_STREAM>(bp[q] + k * B_STEP, st + BM * BK + (q * 4 + wave) * RPC * BK);
   };
@@ -667,19 +679,19 @@ __global__ __launch_bounds__(256, ST * (BM + BN) * BKS * 2 > 80 * 1024 ? 1 : 2) 
 
 int gemm_splits(const GemvArgs& a, Epi epi, int tiles, int nk_all, int num_cus);
 
-template <int BM, int BN, int ST, bool PF, bool PKA, bool PKW, Epi EPI, int BKS = 32>
+template <int BM, int BN, int ST, bool PF, bool PKA, bool PKW, Epi EPI, int BKS = 32, bool GA = false>
 hipError_t launch_ring(GemvArgs& a, int num_cus, hipStream_t s) {
   const int num_m = (a.M + BM - 1) / BM;
   const int cols = EPI == Epi::SiluMul ? BN / 2 : BN;  // gate + up rows per output column
   const int num_n = (a.Nout + cols - 1) / cols;
-  if (a.K % BKS != 0) return hipErrorInvalidValue;
+  if (a.K % BKS != 0 || (GA && (a.K / 2) % BKS != 0)) return hipErrorInvalidValue;
   const int splits = gemm_splits(a, EPI, num_m * num_n, a.K / BKS, num_cus);
   const int total = num_m * num_n * splits;
   const int grid = ((total + 7) / 8) * 8;
   a.grid_x = num_n;
   a.splits = splits;
-  hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, ST, PF, PKA, PKW, EPI, BKS>), dim3(grid), dim3(256), 0, s, a, num_m,
-                     num_n, splits);
+  hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, ST, PF, PKA, PKW, EPI, BKS, GA>), dim3(grid), dim3(256), 0, s, a,
+                     num_m, num_n, splits);
   return hipGetLastError();
 }
 
@@ -774,6 +786,17 @@ hipError_t launch_cfg(GemvArgs& a, int num_cus, hipStream_t s) {
     if (a.M > 16 && a.M <= 256 && !a.ss_out && a.K % 64 == 0 &&
         (EPI == Epi::QkvRope || EPI == Epi::SiluMul || a.part))
       return launch_mid<EPI>(a, num_cus, s);
+  }
+  // The fc input gathered on the fly ([embed[id] ; h] rows) into partials:
+  // the same rings as the plain residual projections, each stage taken from
+  // one half.
+  if constexpr (MODE == AMode::Gather && EPI == Epi::Store) {
+    if (a.part && !a.ss_out) {
+      if (a.M > 256 && (a.K / 2) % 32 == 0)
+        return launch_ring<128, 256, 3, false, false, false, EPI, 32, true>(a, num_cus, s);
+      if (a.M > 16 && (a.K / 2) % 64 == 0)
+        return launch_ring<64, 64, 5, false, false, false, EPI, 64, true>(a, num_cus, s);
+    }
   }
   TileCfg t = pick_tile(a.M, a.Nout, EPI, num_cus);
   // Store / AddTo into split partials: 128 x 128 tiles, K split to fill the CUs
