@@ -217,6 +217,29 @@ def test_forward_bf16_many_sampled_rows(pack):
     _forward_case(wl, pack=pack)
 
 
+@pytest.mark.parametrize("c", [2, 3, 20, 32, 33])
+def test_forward_bf16_row_count_boundaries(c):
+    """Draft-row counts at the projection path boundaries (K = 7, so c * 8
+    rows and c * 7 sampled rows): 16 rows (few-row kernels), 24 (the 64 x 64
+    ring with 64-deep stages), 160 (a 140-row LM head whose second 128-row tile
+    has an all-padding wave pair), 256 (the last row count on the 64 x 64 ring)
+    and 264 (the 128-row ring tiles)."""
+    spec = synth.ModelSpec(hidden=256, vocab=1000, n_layers=1, n_q=8, n_kv=2, head_dim=64, inter=512)
+    wl = synth.Workload(f"rows-c{c}", spec, c=c, K=7, ctx_lo=10, ctx_hi=300, accept_hi=7, seed=120 + c)
+    _forward_case(wl)
+
+
+def test_forward_bf16_widths_off_the_64_grid():
+    """hidden 288 at 160 rows: q/k/v and gate/up (K = 288) are off the 64-wide
+    K grid of the tiled kernels, so the pass takes the unfused plan: the fc
+    input built by its own kernel and projected on the 64 x 64 ring (K = 576),
+    q/k/v and gate/up on the LDS kernel with the rotation and the KV write in
+    their own kernel, o and down on the 64 x 64 ring."""
+    spec = synth.ModelSpec(hidden=288, vocab=700, n_layers=1, n_q=4, n_kv=2, head_dim=64, inter=320)
+    wl = synth.Workload("odd-width-bf16", spec, c=20, K=7, ctx_lo=10, ctx_hi=300, accept_hi=7, seed=131)
+    _forward_case(wl)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_forward_bf16_mid_rows(d):
     """200 draft rows (four 64-row tiles, the last ragged): the LDS-DMA ring
