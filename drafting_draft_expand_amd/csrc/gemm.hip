@@ -434,11 +434,12 @@ __global__ __launch_bounds__(256, BM * BN >= 256 * 256 ? 1 : 2) void gemm_kernel
 
 // ------------------------------------------------------------- LDS-DMA ring
 // The same tiles fed by direct global -> LDS copies (global_load_lds_dwordx4)
-// into a ring of ST LDS stages, one 32-deep K step each; no register staging.
-// A wave's copy instruction writes one contiguous KiB of LDS, 16 tile rows of
-// 64 bytes, lane l landing in row l / 4, chunk l % 4; the lane fetches the
-// global chunk that the row's XOR swizzle places there, so the fragment reads
-// are the register-staged kernel's.
+// into a ring of ST LDS stages, one 32-deep K step each (or two: 64-deep
+// stages); no register staging.  A wave's copy instruction writes one
+// contiguous KiB of LDS, 16 tile rows of 64 bytes, lane l landing in row
+// l / 4, chunk l % 4 (64-deep: 8 rows of 128 bytes, row l / 8, chunk l % 8);
+// the lane fetches the global chunk that the row's XOR swizzle places there,
+// so the fragment reads are the register-staged kernel's.
 //
 // Operand layouts.  Row-major, a copy instruction gathers 16 rows x 64 bytes;
 // tile-major ("packed": [rows / G][K / 32][G][32], G = 256 for W, BM for A,
@@ -752,14 +753,11 @@ hipError_t launch_t(GemvArgs& a, int num_cus, hipStream_t s) {
 // 17..256 rows: the LDS-DMA ring on 64 x 64 tiles with five 64-deep stages
 // (each copy moves 8 rows of 128 bytes, whole cache lines of the row-major
 // operands; 80 KiB of LDS, two workgroups per CU), K split as gemm_splits
-// decides for Store / AddTo into partials.  A stage is waited for as a whole
-// and nearly every stage holds some line that misses L2, so a workgroup moves
-// about (stages - 2) x 16 KiB per memory round trip; two workgroups per CU
-// with five stages keep the most bytes in flight.  Qwen-shaped layer at
-// c = 16 (cold weights): steps 302 / 311 / 338 -> 287 / 301 / 332 us at
-// K = 3 / 5 / 7 against the register-staged 128-row tiles; wider tiles
-// (96 to 256 columns, one workgroup per CU, more K splits) and six stages
-// ran slower.
+// decides for Store / AddTo into partials.  Qwen-shaped layer at c = 16
+// (cold weights): steps 302 / 311 / 338 -> 287 / 301 / 332 us at K = 3 / 5 / 7
+// against the register-staged 128-row tiles; with 32-deep stages (half cache
+// lines per copy) the K = 7 step was 354 us, and wider tiles (96 to 256
+// columns, one workgroup per CU, more K splits) and six stages ran slower.
 template <Epi EPI>
 hipError_t launch_mid(GemvArgs& a, int num_cus, hipStream_t s) {
   return launch_ring<64, 64, 5, false, false, false, EPI, 64>(a, num_cus, s);
