@@ -217,6 +217,36 @@ def test_forward_bf16_many_sampled_rows(pack):
     _forward_case(wl, pack=pack)
 
 
+def _random_case(seed):
+    """A bf16 drafter and batch drawn from a seeded generator: widths on and off
+    the 64-wide K grid, 16- to 128-dim heads, GQA groups of 1-8, one or two
+    layers, 1-40 sequences, K = 1-8, contexts up to ~1000 tokens, packed or
+    not; the shape fixes which projection, attention and LM-head kernels run."""
+    r = np.random.default_rng(np.random.SeedSequence([seed, 9901]))
+    d = int(r.choice([16, 32, 64, 128]))
+    n_kv = int(r.choice([1, 2, 4]))
+    n_q = n_kv * int(r.choice([1, 2, 4, 8]))
+    spec = synth.ModelSpec(hidden=int(r.choice([64, 128, 160, 192, 256, 288, 320, 384, 416, 448, 512])),
+                           vocab=int(r.integers(300, 3001)), n_layers=int(r.choice([1, 2])), n_q=n_q, n_kv=n_kv,
+                           head_dim=d, inter=int(r.choice([96, 128, 224, 256, 320, 352, 448, 512, 640])))
+    K = int(r.integers(1, 9))
+    lo = int(r.integers(0, 201))
+    wl = synth.Workload(f"random-{seed}", spec, c=int(r.integers(1, 41)), K=K, ctx_lo=lo,
+                        ctx_hi=lo + int(r.integers(0, 801)), accept_hi=K, seed=2000 + seed)
+    return wl, bool(r.integers(0, 2))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_forward_bf16_random_shapes(seed):
+    """Seeded sweep over drafter and batch shapes (see _random_case), each
+    against the oracle like the fixed cases."""
+    wl, pack = _random_case(seed)
+    s = wl.model
+    _say(f"random case {seed}: H={s.hidden} V={s.vocab} layers={s.n_layers} q/kv={s.n_q}/{s.n_kv} d={s.head_dim} "
+         f"I={s.inter} c={wl.c} K={wl.K} ctx={wl.ctx_lo}..{wl.ctx_hi} pack={pack}")
+    _forward_case(wl, pack=pack)
+
+
 @pytest.mark.parametrize("c", [2, 3, 20, 32, 33])
 def test_forward_bf16_row_count_boundaries(c):
     """Draft-row counts at the projection path boundaries (K = 7, so c * 8
