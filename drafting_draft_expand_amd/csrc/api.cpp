@@ -34,9 +34,12 @@ Timing g_timing[kTimingClasses];
 }  // namespace
 
 // Packed copies of the projection weights (caller-owned buffer attached by
-// pe_model_pack_weights), read by the weight-streaming MFMA kernel.
+// pe_model_pack_weights): fragment order for the weight-streaming MFMA kernel
+// (qkv .. down), tile-major in the ring's load order for passes over more
+// than 256 rows (t_*, null when the shapes do not take that route).
 struct PackedLayer {
   const void *qkv, *o, *gate, *up, *down;
+  const void *t_qkv, *t_o, *t_gu, *t_down;
 };
 
 struct pe_model {
@@ -44,6 +47,7 @@ struct pe_model {
   pe_weights w;
   std::vector<pe_layer_weights> layers;
   const void* pk_fc = nullptr;
+  const void* pk_fc_tiles = nullptr;   // tile-major fc (passes over > 256 rows)
   std::vector<PackedLayer> pk_layers;  // empty: not packed
   const void* pk_lm = nullptr;         // tile-major LM head (packed models)
   int num_cus = 256;  // compute units of the device current at create
@@ -96,11 +100,14 @@ Workspace plan_workspace(const pe_model* m, int c, int K, int N) {
   w.lm_parts = 4096;  // upper bound on LM-head workgroups (grid is capped at 2 per CU)
   size_t off = 0;
   w.x = off;         off += align_up(size_t(N) * H * 4);
-  w.act = off;       off += align_up(size_t(N) * act_cols * eb);
+  // (act and mlp rounded up to 128 rows: over > 256 rows they may be written
+  // tile-major in 128-row groups)
+  const size_t Np = size_t(N + 127) / 128 * 128;
+  w.act = off;       off += align_up(Np * act_cols * eb);
   w.qkv = off;       off += align_up(size_t(N) * (qd + 2 * kvd) * 4);
   w.q = off;         off += align_up(size_t(N) * qd * eb);
   w.attn_part = off; off += align_up(size_t(N) * d.n_q * w.splits * (d.head_dim + 2) * 4);
-  w.mlp = off;       off += align_up(size_t(N) * d.inter * eb);
+  w.mlp = off;       off += align_up(Np * d.inter * eb);
   w.top2 = off;      off += align_up(size_t(S) * w.lm_parts * sizeof(pe::Top2));
   // (rounded up to 128 rows: the LM head may read it tile-major in 128-row groups)
   w.f = off;         off += align_up(size_t((S + 127) / 128 * 128) * H * eb);
@@ -272,13 +279,55 @@ void pack_plan(const pe_model* m, std::vector<pe::PackArgs>& v) {
 }
 }  // namespace
 
+namespace {
+// Tile-major copies for the ring GEMM over more than 256 rows, in buffer
+// order: fc, then per layer q/k/v, o, gate/up, down.  Only when every
+// projection takes the tiled route there (bf16, each K a multiple of 64), as
+// the producers of their operands then write them tile-major too.
+bool many_rows_tiles(const pe_model_desc& d) {
+  const int qd = d.n_q * d.head_dim;
+  return d.dtype == PE_BF16 && d.n_layers > 0 && d.hidden % 64 == 0 && qd % 64 == 0 && d.inter % 64 == 0;
+}
+struct TileCopy {
+  pe::Epi epi;
+  pe::GemvArgs g;
+};
+void tile_plan(const pe_model* m, std::vector<TileCopy>& v) {
+  v.clear();
+  const pe_model_desc& d = m->d;
+  if (!many_rows_tiles(d)) return;
+  const int H = d.hidden, qd = d.n_q * d.head_dim, kvd = d.n_kv * d.head_dim, I = d.inter;
+  auto one = [](pe::Epi e, const void* a, const void* b, const void* c, int n_a, int n_b, int nout, int k,
+                int rope_d) {
+    TileCopy t{};
+    t.epi = e;
+    t.g.w_a = a; t.g.w_b = b; t.g.w_c = c; t.g.n_a = n_a; t.g.n_b = n_b; t.g.Nout = nout; t.g.K = k;
+    t.g.rope.d = rope_d;
+    return t;
+  };
+  v.push_back(one(pe::Epi::Store, m->w.w_fc, m->w.w_fc, m->w.w_fc, H, 0, H, 2 * H, 0));
+  for (int l = 0; l < d.n_layers; ++l) {
+    const pe_layer_weights& L = m->layers[l];
+    v.push_back(one(pe::Epi::QkvRope, L.wq, L.wk, L.wv, qd, kvd, qd + 2 * kvd, H, d.head_dim));
+    v.push_back(one(pe::Epi::AddTo, L.wo, L.wo, L.wo, H, 0, H, qd, 0));
+    v.push_back(one(pe::Epi::SiluMul, L.w_gate, L.w_up, L.w_up, I, I, I, H, 0));
+    v.push_back(one(pe::Epi::AddTo, L.w_down, L.w_down, L.w_down, H, 0, H, I, 0));
+  }
+}
+}  // namespace
+
 size_t pe_packed_weights_bytes(const pe_model* m) {
   if (!m) return 0;
   size_t total = 0;
   std::vector<pe::PackArgs> plan;
   pack_plan(m, plan);
   for (const pe::PackArgs& p : plan) total += align_up(pe::packed_bytes(p.Nout, p.K));
-  if (!plan.empty()) total += align_up(pe::packed_tile_bytes(m->d.vocab, m->d.hidden));
+  if (!plan.empty()) {
+    total += align_up(pe::packed_tile_bytes(m->d.vocab, m->d.hidden));
+    std::vector<TileCopy> tiles;
+    tile_plan(m, tiles);
+    for (const TileCopy& t : tiles) total += align_up(pe::proj_tile_bytes(t.epi, t.g.Nout, t.g.K));
+  }
   return total;
 }
 
@@ -298,12 +347,28 @@ pe_status pe_model_pack_weights(pe_model* m, void* packed, size_t packed_bytes, 
     b += align_up(pe::packed_bytes(p.Nout, p.K));
   }
   PE_HIP(pe::launch_pack_tiles(m->w.w_lm, m->d.vocab, m->d.hidden, b, stream));
-  m->pk_lm = b;
+  const void* lm = b;
+  b += align_up(pe::packed_tile_bytes(m->d.vocab, m->d.hidden));
+  std::vector<TileCopy> tiles;
+  tile_plan(m, tiles);
+  std::vector<const void*> tdst;
+  for (const TileCopy& t : tiles) {
+    PE_HIP(pe::launch_pack_proj_tiles(t.epi, t.g, b, stream));
+    tdst.push_back(b);
+    b += align_up(pe::proj_tile_bytes(t.epi, t.g.Nout, t.g.K));
+  }
+  m->pk_lm = lm;
   m->pk_fc = dst[0];
+  m->pk_fc_tiles = tdst.empty() ? nullptr : tdst[0];
   m->pk_layers.assign(m->d.n_layers, PackedLayer{});
   for (int l = 0; l < m->d.n_layers; ++l) {
     const void* const* q = dst.data() + 1 + 5 * l;
-    m->pk_layers[l] = PackedLayer{q[0], q[1], q[2], q[3], q[4]};
+    PackedLayer P{q[0], q[1], q[2], q[3], q[4], nullptr, nullptr, nullptr, nullptr};
+    if (!tdst.empty()) {
+      const void* const* t = tdst.data() + 1 + 4 * l;
+      P.t_qkv = t[0]; P.t_o = t[1]; P.t_gu = t[2]; P.t_down = t[3];
+    }
+    m->pk_layers[l] = P;
   }
   return PE_OK;
 }
@@ -451,6 +516,12 @@ pe_status forward_impl(const pe_model* m, int32_t c, int32_t K, int32_t N, const
   // packed models split the down projection instead (the final RMSNorm adds
   // its partials for the sampled rows)
   const bool fnorm = fused && !packed && fused_final_norm(d, N, S);
+  // Over more than 256 rows every projection reads a tile-major copy of its
+  // weights, and the producers of the plain operands (both RMSNorms, the
+  // attention merge, the SiluMul epilogue) write them tile-major in 128-row
+  // groups, so that each copy into LDS reads one contiguous KiB of either.
+  const bool many = fused && packed && N > 256 && m->pk_fc_tiles;
+  const int og = many ? 128 : 0;
   // attention and LM head are shared by both plans
   auto attention = [&](int l) -> pe_status {
     pe::AttnArgs at{};
@@ -458,7 +529,7 @@ pe_status forward_impl(const pe_model* m, int32_t c, int32_t K, int32_t N, const
     at.block_size = d.block_size; at.max_blocks = max_blocks; at.splits = ws.splits; at.dtype = t;
     at.q = qrot; at.pos = draft_pos; at.rejected = is_rejected; at.cu_draft = cu_draft;
     at.kv_lens = kv_lens; at.block_table = block_table; at.k_cache = k_cache[l];
-    at.v_cache = v_cache[l]; at.partial = part; at.out = act;
+    at.v_cache = v_cache[l]; at.partial = part; at.out = act; at.out_group = og;
     TimedScope ts(PE_KERNEL_ATTENTION, stream, timed);
     PE_HIP(pe::launch_attention(at, stream));
     return PE_OK;
@@ -490,7 +561,7 @@ pe_status forward_impl(const pe_model* m, int32_t c, int32_t K, int32_t N, const
       rt.pos = draft_pos; rt.out = rope_tab; rt.half = d.head_dim / 2; rt.freq = m->freq;
     }
     PE_HIP(pe::launch_rmsnorm(t, N, H, nullptr, x, gain, d.rms_eps, act, stream, live, xpart, pend_splits, N,
-                              pend_acc, 0, rope_table ? &rt : nullptr));
+                              pend_acc, og, rope_table ? &rt : nullptr));
     pend_splits = 0;
     return PE_OK;
   };
@@ -504,6 +575,7 @@ pe_status forward_impl(const pe_model* m, int32_t c, int32_t K, int32_t N, const
       g.ids = draft_ids; g.embed = m->w.embed; g.x2 = draft_hidden;
       g.w_a = g.w_b = g.w_c = m->w.w_fc; g.n_a = H; g.n_b = 0;
       g.pk_a = packed ? m->pk_fc : nullptr;
+      g.pk_tiles = many ? m->pk_fc_tiles : nullptr;
       g.y = x; g.ldy = H;
       if ((st = into_x(g, pe::Epi::Store)) != PE_OK) return st;
     }
@@ -519,6 +591,7 @@ pe_status forward_impl(const pe_model* m, int32_t c, int32_t K, int32_t N, const
         g.M = N; g.m_live = live; g.Nout = qd + 2 * kvd; g.K = H; g.amode = pe::AMode::Plain; g.x = act;
         g.w_a = L.wq; g.n_a = qd; g.w_b = L.wk; g.n_b = kvd; g.w_c = L.wv;
         g.pk_a = P ? P->qkv : nullptr;
+        g.pk_tiles = many ? P->t_qkv : nullptr; g.x_group = og;
         g.rope.n_q = d.n_q; g.rope.n_kv = d.n_kv; g.rope.d = d.head_dim; g.rope.block_size = d.block_size;
         g.rope.slot = slot_mapping;
         g.rope.rejected = is_rejected; g.rope.q_out = qrot; g.rope.k_cache = k_cache[l];
@@ -531,6 +604,7 @@ pe_status forward_impl(const pe_model* m, int32_t c, int32_t K, int32_t N, const
         g.M = N; g.m_live = live; g.Nout = H; g.K = qd; g.amode = pe::AMode::Plain; g.x = act;
         g.w_a = g.w_b = g.w_c = L.wo; g.n_a = H; g.n_b = 0;
         g.pk_a = P ? P->o : nullptr;
+        g.pk_tiles = many ? P->t_o : nullptr; g.x_group = og;
         g.y = x; g.ldy = H;
         if ((st = into_x(g, pe::Epi::AddTo)) != PE_OK) return st;
       }
@@ -540,7 +614,8 @@ pe_status forward_impl(const pe_model* m, int32_t c, int32_t K, int32_t N, const
         g.M = N; g.m_live = live; g.Nout = d.inter; g.K = H; g.amode = pe::AMode::Plain; g.x = act;
         g.w_a = L.w_gate; g.w_b = L.w_up; g.w_c = L.w_up; g.n_a = d.inter; g.n_b = d.inter;
         g.pk_a = P ? P->gate : nullptr; g.pk_b = P ? P->up : nullptr;
-        g.y_op = mlp; g.ldy = d.inter;
+        g.pk_tiles = many ? P->t_gu : nullptr; g.x_group = og;
+        g.y_op = mlp; g.ldy = d.inter; g.y_group = og;
         if ((st = proj(g, pe::Epi::SiluMul)) != PE_OK) return st;
       }
       {
@@ -548,6 +623,7 @@ pe_status forward_impl(const pe_model* m, int32_t c, int32_t K, int32_t N, const
         g.M = N; g.m_live = live; g.Nout = H; g.K = d.inter; g.amode = pe::AMode::Plain; g.x = mlp;
         g.w_a = g.w_b = g.w_c = L.w_down; g.n_a = H; g.n_b = 0;
         g.pk_a = P ? P->down : nullptr;
+        g.pk_tiles = many ? P->t_down : nullptr; g.x_group = og;
         g.y = x; g.ldy = H; g.ss_out = fnorm && l == d.n_layers - 1 ? ss0 : nullptr;
         if ((st = into_x(g, pe::Epi::AddTo)) != PE_OK) return st;
       }

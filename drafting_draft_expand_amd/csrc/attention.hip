@@ -660,7 +660,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   for (int hh = 0; hh < HPW; ++hh) {
     const int h = h0 + hh;
     if (h >= a.n_q) break;
-    T* out = static_cast<T*>(a.out) + (static_cast<int64_t>(row) * a.n_q + h) * D;
+    // element h D + e of the row: row-major, or tile-major in groups of
+    // out_group rows (32-element pieces of one row contiguous)
+    const int G = a.out_group;
+    auto out_at = [&](int e) -> int64_t {
+      const int64_t k = static_cast<int64_t>(h) * D + e;
+      if (G == 0) return static_cast<int64_t>(row) * a.n_q * D + k;
+      return (static_cast<int64_t>(row / G) * (a.n_q * D / 32) + k / 32) * G * 32 + (row % G) * 32 + (k & 31);
+    };
+    T* out = static_cast<T*>(a.out);
     // (a rejected row's partials were never written: they are read with the
     // rest, so no load waits for the flag, and discarded)
     const float* p = a.partial + (static_cast<int64_t>(row) * a.n_q + h) * S * (D + 2);
@@ -690,7 +698,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     const float inv = 1.f / den;
 #pragma unroll
     for (int e = 0; e < DV; ++e)
-      if (lane + 64 * e < D) out[lane + 64 * e] = Elem<T>::from_f32(rejected ? 0.f : num[e] * inv);
+      if (lane + 64 * e < D) out[out_at(lane + 64 * e)] = Elem<T>::from_f32(rejected ? 0.f : num[e] * inv);
   }
 }
 
@@ -755,6 +763,7 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+  if (a.out_group < 0 || (a.out_group > 0 && (a.n_q * a.d) % 32 != 0)) return hipErrorInvalidValue;
   return a.dtype == DType::F32 ? launch_t<float>(a, s) : launch_t<bf16_t>(a, s);
 }
 

@@ -111,8 +111,12 @@ __device__ __forceinline__ void tile_epilogue(const GemvArgs& a, f32x4 (&acc)[TM
           if (m >= a.M || n >= a.Nout) continue;
           const float gt = acc[i][jn][q];
           const float sg = gt / (1.f + expf(-gt));
-          static_cast<bf16_t*>(a.y_op)[static_cast<int64_t>(m) * a.ldy + n] =
-              f32_to_bf16(sg * acc[i][jn + TN / 2][q]);
+          // row-major, or tile-major in 128-row groups for a consumer that
+          // reads its A operand that way
+          const int64_t at = a.y_group ? (static_cast<int64_t>(m >> 7) * a.Nout + (n & ~31)) * 128 + (m & 127) * 32 +
+                                             (n & 31)
+                                       : static_cast<int64_t>(m) * a.ldy + n;
+          static_cast<bf16_t*>(a.y_op)[at] = f32_to_bf16(sg * acc[i][jn + TN / 2][q]);
         }
       }
   } else if constexpr (EPI == Epi::QkvRope) {
@@ -477,8 +481,8 @@ __global__ __launch_bounds__(256, ST * (BM + BN) * BKS * 2 > 80 * 1024 ? 1 : 2) 
   static_assert(!GA || (!PKA && !PF), "gathered A rows are row-major");
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 16, TN = WN / 16;
-  static_assert(!PKW || EPI == Epi::Argmax || EPI == Epi::Store || EPI == Epi::AddTo,
-                "the tile-major copy holds W rows in plain order");
+  // PKW: the tile-major copy holds W rows in the order the N tiles load them
+  // (plain for the LM head, Store and AddTo; launch_pack_proj_tiles for all)
   static_assert(BM % (4 * RPC) == 0 && BN % (4 * RPC) == 0, "whole copy blocks for every wave");
   static_assert(!PKW || kTileGroup % BN == 0, "a W tile lies inside one packed row group");
   constexpr int IA = BM / (4 * RPC), IB = BN / (4 * RPC);  // copy instructions per wave and stage
@@ -555,9 +559,10 @@ __global__ __launch_bounds__(256, ST * (BM + BN) * BKS * 2 > 80 * 1024 ? 1 : 2) 
   // The LM head over at most 128 rows (the instance without fragment
   // prefetch) has one M tile, so each W tile is read exactly once: its copies
   // are non-temporal and leave the caches to the rows (Qwen-shaped head over
-  // 112 rows: step 0.378-0.385 -> 0.351-0.357 ms).  With several M tiles the
-  // W tiles are shared through L2 and keep the default policy.
-  constexpr bool W_STREAM = PKW && !PF;
+  // 112 rows: step 0.378-0.385 -> 0.351-0.357 ms).  With several M tiles (and
+  // in the layer projections) the W tiles are shared through L2 and keep the
+  // default policy.
+  constexpr bool W_STREAM = PKW && !PF && EPI == Epi::Argmax;
   auto request = [&](int kt, auto s_c) __attribute__((always_inline)) {
     bf16_t* st = ring(s_c);
     const int64_t k = kbase + min(kt, nk - 1);
@@ -763,8 +768,45 @@ hipError_t launch_mid(GemvArgs& a, int num_cus, hipStream_t s) {
   return launch_ring<64, 64, 5, false, false, false, EPI, 64>(a, num_cus, s);
 }
 
+// Tile widths of the projections over more than 256 rows: 128 x 128 for
+// q/k/v (the rotary epilogue spills on the wider tile), 128 x 256 for the
+// rest.  The tile-major weight copies (launch_pack_proj_tiles) are packed in
+// the load order of exactly these tiles.
+template <Epi EPI>
+constexpr int kManyRowsBN = EPI == Epi::QkvRope ? 128 : 256;
+
+// Projections over more than 256 rows with the weights' tile-major copy and,
+// for a plain operand, A written tile-major in 128-row groups by its producer
+// (RMSNorm, attention merge, SiluMul epilogue): each copy instruction of the
+// ring then reads one contiguous KiB of either operand.  Anything else is
+// refused rather than run on a layout the kernel does not read.
+template <Epi EPI, AMode MODE>
+hipError_t launch_many_rows_packed(GemvArgs& a, int num_cus, hipStream_t s) {
+  if (!a.pk_tiles || a.M <= 256 || a.ss_out) return hipErrorInvalidValue;
+  if (a.y_group != 0 && (EPI != Epi::SiluMul || a.y_group != 128 || a.Nout % 32 != 0)) return hipErrorInvalidValue;
+  if constexpr (MODE == AMode::Gather) {
+    if constexpr (EPI == Epi::Store) {
+      if (!a.part || a.x_group != 0) return hipErrorInvalidValue;
+      return launch_ring<128, 256, 3, false, false, true, EPI, 32, true>(a, num_cus, s);
+    }
+    return hipErrorInvalidValue;
+  } else {
+    if (a.x_group != 128) return hipErrorInvalidValue;
+    if constexpr (EPI == Epi::QkvRope || EPI == Epi::SiluMul)
+      return launch_ring<128, kManyRowsBN<EPI>, EPI == Epi::QkvRope ? 4 : 3, false, true, true, EPI>(a, num_cus, s);
+    else if constexpr (EPI == Epi::AddTo) {
+      if (!a.part) return hipErrorInvalidValue;
+      return launch_ring<128, 256, 3, false, true, true, EPI>(a, num_cus, s);
+    }
+    return hipErrorInvalidValue;
+  }
+}
+
 template <Epi EPI, AMode MODE>
 hipError_t launch_cfg(GemvArgs& a, int num_cus, hipStream_t s) {
+  if constexpr (EPI != Epi::Argmax) {
+    if (a.pk_tiles || a.x_group || a.y_group) return launch_many_rows_packed<EPI, MODE>(a, num_cus, s);
+  }
   // Many rows (more than two 128-row tiles) on a plain operand: the LDS-DMA
   // ring on row-major W -- 128 x 256 tiles (K split when the caller takes
   // partials), 128 x 128 for q/k/v (the rotary epilogue spills on the wider
@@ -825,7 +867,63 @@ __global__ void pack_tiles_kernel(const bf16_t* __restrict__ w, bf16_t* __restri
   }
 }
 
+// Tile-major copy of a projection in its ring tiles' load order: packed row
+// R is row R % BN of N tile R / BN (b_ptr, which clamps past the last W row),
+// rows past the last tile zero; layout and thread mapping as pack_tiles_kernel
+template <Epi EPI, int BN>
+__global__ void pack_proj_tiles_kernel(GemvArgs a, bf16_t* __restrict__ dst, int rows, int64_t chunks) {
+  const int nk = a.K / 32;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < chunks;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int c = static_cast<int>(i & 3);
+    const int64_t rest = i >> 2;
+    const int r = static_cast<int>(rest % kTileGroup);
+    const int64_t rest2 = rest / kTileGroup;
+    const int kt = static_cast<int>(rest2 % nk);
+    const int64_t row = (rest2 / nk) * kTileGroup + r;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (row < rows)
+      v = load16(b_ptr<EPI, BN, BN / 2>(a, static_cast<int>(row / BN), static_cast<int>(row % BN)) + kt * 32 + c * 8);
+    store16(dst + i * 8, v);
+  }
+}
+
+// rows the ring's N tiles load over > 256 rows (whole tiles)
+int many_rows_tile_rows(Epi epi, int Nout) {
+  const int bn = epi == Epi::QkvRope ? kManyRowsBN<Epi::QkvRope> : kManyRowsBN<Epi::Store>;
+  const int cols = epi == Epi::SiluMul ? bn / 2 : bn;
+  return (Nout + cols - 1) / cols * bn;
+}
+
+template <Epi EPI>
+hipError_t pack_proj_t(const GemvArgs& a, void* dst, hipStream_t s) {
+  const int rows = many_rows_tile_rows(EPI, a.Nout);
+  const int64_t chunks = static_cast<int64_t>(proj_tile_bytes(EPI, a.Nout, a.K) / 16);
+  const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, 16384);
+  hipLaunchKernelGGL((pack_proj_tiles_kernel<EPI, kManyRowsBN<EPI>>), dim3(static_cast<unsigned>(blocks)), dim3(256),
+                     0, s, a, static_cast<bf16_t*>(dst), rows, chunks);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+size_t proj_tile_bytes(Epi epi, int Nout, int K) {
+  const int rows = many_rows_tile_rows(epi, Nout);
+  return static_cast<size_t>((rows + kTileGroup - 1) / kTileGroup) * kTileGroup * K * 2;
+}
+
+hipError_t launch_pack_proj_tiles(Epi epi, const GemvArgs& a, void* dst, hipStream_t s) {
+  if (!dst || !a.w_a || !a.w_b || !a.w_c || a.Nout <= 0 || a.K <= 0 || a.K % 32 != 0) return hipErrorInvalidValue;
+  switch (epi) {
+    case Epi::Store:
+    case Epi::AddTo: return pack_proj_t<Epi::AddTo>(a, dst, s);
+    case Epi::SiluMul: return pack_proj_t<Epi::SiluMul>(a, dst, s);
+    case Epi::QkvRope:
+      if (a.rope.d != 16 && a.rope.d != 32 && a.rope.d != 64 && a.rope.d != 128) return hipErrorInvalidValue;
+      return pack_proj_t<Epi::QkvRope>(a, dst, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 size_t packed_tile_bytes(int Nout, int K) {
   return static_cast<size_t>((Nout + kTileGroup - 1) / kTileGroup) * kTileGroup * K * 2;

@@ -709,6 +709,8 @@ hipError_t launch_gemv(GemvArgs& a, Epi epi, DType dt, int num_cus, hipStream_t 
   a.splits = 1;
   if (epi == Epi::QkvRope && !a.rope.table) return hipErrorInvalidValue;
   if (proj_kernel(a.M, a.K, dt, epi) == ProjKernel::Tiled) return launch_gemm(a, epi, num_cus, s);
+  // tile-major operands and outputs are read and written by the tiled kernels only
+  if (a.x_group || a.y_group || (a.pk_tiles && epi != Epi::Argmax)) return hipErrorInvalidValue;
   if (use_mfma(a.M, a.K, dt, epi)) {
     if (a.amode == AMode::Plain) {
       switch (epi) {

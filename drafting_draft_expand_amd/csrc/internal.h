@@ -110,8 +110,9 @@ struct GemvArgs {
   // the weight-streaming MFMA kernel when set: pk_a for all Nout rows (the gate
   // for SiluMul), pk_b the up projection
   const void *pk_a, *pk_b;
-  // tile-major copy of the rows for the tiled GEMM's argmax epilogue (LM head):
-  // [ceil(Nout / 256)][K / 32][256][32], rows past Nout zero (launch_pack_tiles)
+  // tile-major copy of W for the ring GEMM: the LM head's rows in order
+  // (launch_pack_tiles), or a layer projection's rows in the order its ring
+  // tiles load them (launch_pack_proj_tiles); [rows / 256][K / 32][256][32]
   const void* pk_tiles;
   // x tile-major in groups of x_group rows ([M / G][K / 32][G][32], rows past M
   // present), 0: row-major; only with pk_tiles, and only G = 128
@@ -120,6 +121,9 @@ struct GemvArgs {
   float* y;                    // Store / AddTo: fp32 [M, ldy]
   void* y_op;                  // SiluMul: model dtype [M, ldy]
   int ldy;
+  // SiluMul: y_op tile-major in groups of y_group rows ([M / G][Nout / 32][G][32],
+  // Nout % 32 == 0), 0: row-major; only G = 128
+  int y_group;
   float* ss_out;               // Store / AddTo (MFMA kernel): [Nout / 16, M] row sums of y^2 per 16-column tile
   // Store / AddTo on packed weights without ss_out: when set, the kernel may
   // split K over `splits` workgroups and leave part[z][m][n] (stride ldy)
@@ -160,6 +164,15 @@ hipError_t launch_pack(const PackArgs& p, hipStream_t s);
 // 256-row groups, each 32-deep K step of a group one contiguous 16 KiB block.
 size_t packed_tile_bytes(int Nout, int K);
 hipError_t launch_pack_tiles(const void* w, int Nout, int K, void* dst, hipStream_t s);
+// Tile-major copy of a layer projection for the ring GEMM over more than 256
+// rows (Store / AddTo / SiluMul / QkvRope): packed row R holds the W row that
+// row R % BN of the ring's N tile R / BN loads (q/k/v in rotary-pair order,
+// gate and up rows interleaved as the SiluMul tile pairs them), in the layout
+// of launch_pack_tiles.  `a` carries the W pointers and shape (w_a/w_b/w_c,
+// n_a, n_b, Nout, K, rope.d).  The copy fits only the tile width the launcher
+// uses for that epilogue over > 256 rows.
+size_t proj_tile_bytes(Epi epi, int Nout, int K);
+hipError_t launch_pack_proj_tiles(Epi epi, const GemvArgs& a, void* dst, hipStream_t s);
 
 // ---------------------------------------------------------------- small kernels
 hipError_t launch_build_fc_input(DType dt, int N, int H, const int32_t* ids, const void* embed,
@@ -204,6 +217,9 @@ struct AttnArgs {
   const void *k_cache, *v_cache;
   float* partial;               // [N, n_q, splits, d + 2]
   void* out;                    // [N, n_q d] model dtype
+  // out tile-major in groups of out_group rows ([N / G][n_q d / 32][G][32],
+  // n_q d % 32 == 0), 0: row-major
+  int out_group;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 

@@ -123,8 +123,10 @@ pe_status pe_model_create(const pe_model_desc *desc, const pe_weights *weights, 
 void pe_model_destroy(pe_model *model);
 
 /* Bytes of device memory for the packed copies of the weights: the projection
- * weights (fc and every layer's q/k/v, o, gate, up, down) and the LM head
- * (vocab rounded up to 256 rows x hidden); 0 when the model has nothing to
+ * weights (fc and every layer's q/k/v, o, gate, up, down) in fragment order,
+ * the LM head (vocab rounded up to 256 rows x hidden), and, when hidden,
+ * n_q*head_dim and inter are multiples of 64, the projections once more in
+ * tile order (outputs rounded up to whole tiles); 0 when the model has nothing to
  * pack (fp32 weights, no layers, or hidden / n_q*head_dim / inter not
  * multiples of 32 or head_dim not a multiple of 16). */
 size_t pe_packed_weights_bytes(const pe_model *model);
@@ -134,7 +136,10 @@ size_t pe_packed_weights_bytes(const pe_model *model);
  * fragment one contiguous KiB, the q/k/v rows grouped in rotary pairs), read
  * with few draft rows (at most 16 rows per pass, e.g. one sequence at K <= 8),
  * and the LM head tile-major (256-row groups, each 32-deep slice of a group one
- * contiguous 16 KiB block), read when more than 16 rows are sampled; attaches
+ * contiguous 16 KiB block), read when more than 16 rows are sampled, and the
+ * projections tile-major in the same layout, their rows in the order the
+ * 128 x 256 (q/k/v: 128 x 128) tiles load them, read by passes over more than
+ * 256 draft rows (whose activations are then also kept tile-major); attaches
  * the buffer to the model.  From then on those products stream the copies
  * instead of the row-major weights (same products, same results up to the
  * summation order of split partial sums).  `packed`: device buffer of at least
@@ -146,8 +151,9 @@ size_t pe_packed_weights_bytes(const pe_model *model);
  * Memory cost: the copies add to the caller's row-major weights, which stay
  * in use (the LM head over at most 16 sampled rows, the embedding, the norms);
  * for a GPT-OSS-20B-shaped drafter (hidden 2880, vocab 201088) that is
- * 219 MB of projections plus 1.16 GB for the LM head, so the drafter's weight
- * footprint grows from 1.38 GB to about 2.76 GB.
+ * 219 MB of projections in fragment order, 226 MB in tile order and 1.16 GB
+ * for the LM head, so the drafter's weight footprint grows from 1.38 GB to
+ * about 2.99 GB.
  * Returns PE_OK (nothing to do when 0 bytes are needed), PE_EINVAL (null or
  * misaligned buffer), PE_EWORKSPACE (too small), PE_EHIP. */
 pe_status pe_model_pack_weights(pe_model *model, void *packed, size_t packed_bytes, hipStream_t stream);
