@@ -391,20 +391,22 @@ __global__ __launch_bounds__(512, OCC) void attn_mfma_kernel(AttnArgs a) {
 // V (one KiB each; eight keys never straddle a 16-token page).  Step t waits
 // until its own copies of stage t have landed (ST-2 stages still in flight),
 // meets the other waves, requests tile t+ST-1 into the slot step t-1 used,
-// then computes.  64-dim heads fit two workgroups per CU, 128-dim heads one.
+// then computes.  Two stages (ST = 2) make it a double buffer: every copy of
+// tile t has landed before the barrier of step t.  64-dim heads with three
+// stages and 128-dim heads with two fit two workgroups per CU.
 template <int D, int ST>
-__global__ __launch_bounds__(512, D == 64 ? 4 : 2) void attn_ring_kernel(AttnArgs a) {
+__global__ __launch_bounds__(512, D == 64 || ST == 2 ? 4 : 2) void attn_ring_kernel(AttnArgs a) {
   constexpr int KT = 64, PL = D / 64;  // keys per tile, 64-dim planes
   constexpr int DT = D / 16, KK = D / 32;
   constexpr int SK = KT * D;  // elements of one K (or V) tile
   constexpr int SP = KT * 64;  // elements of one plane of a tile
   constexpr int BS = 16;       // KV page size (the only one the library accepts)
   static_assert(D == 64 || D == 128, "64- or 128-dim heads");
-  static_assert(ST >= 3 && ST <= 4, "three or four ring stages");
+  static_assert(ST >= 2 && ST <= 4, "two to four ring stages");
   typedef short v4i16 __attribute__((ext_vector_type(4)));
   __shared__ __attribute__((aligned(16))) bf16_t R0[2 * SK];
   __shared__ __attribute__((aligned(16))) bf16_t R1[2 * SK];
-  __shared__ __attribute__((aligned(16))) bf16_t R2[2 * SK];
+  __shared__ __attribute__((aligned(16))) bf16_t R2[ST > 2 ? 2 * SK : 8];
   __shared__ __attribute__((aligned(16))) bf16_t R3[ST > 3 ? 2 * SK : 8];
   __shared__ int32_t pages[kAttnMaxPages];
   auto ring = [&](auto s_c) __attribute__((always_inline)) -> bf16_t* {
@@ -707,10 +709,13 @@ void launch_mfma(const AttnArgs& a, dim3 grid, hipStream_t s) {
   // The LDS-DMA ring whenever a split's page numbers fit in LDS, else the
   // register-staged kernel reading the block table (64-dim heads: two
   // workgroups per CU; 128-dim heads: one, with a deeper register prefetch,
-  // as two would spill)
+  // as two would spill).  The ring keeps three stages for 64-dim heads; for
+  // 128-dim heads two stages (68 KiB of LDS, at most 128 VGPRs) let two
+  // workgroups share a CU where three stages fit only one (Qwen-shaped c=16,
+  // K=7: 79.8 -> 77.8 us).
   constexpr int DEPTH = D == 64 ? 2 : 3, OCC = D == 64 ? 4 : 2;
   if (a.max_blocks <= (kAttnMaxPages - 8) * a.splits)
-    hipLaunchKernelGGL((attn_ring_kernel<D, 3>), grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL((attn_ring_kernel<D, D == 128 ? 2 : 3>), grid, dim3(512), 0, s, a);
   else
     hipLaunchKernelGGL((attn_mfma_kernel<D, DEPTH, OCC, false>), grid, dim3(512), 0, s, a);
 }
