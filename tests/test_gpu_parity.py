@@ -334,6 +334,13 @@ def test_forward_gptoss_c64_full():
     _forward_case(synth.WORKLOADS["gptoss20b-bf16-c64-k7"])
 
 
+def test_forward_gptoss_c64_k8_full():
+    """All 64 sequences at K=8: 1024 draft rows (eight whole 128-row groups of
+    the tile-major operands) and 512 sampled rows (four LM-head row tiles, none
+    of them padded)."""
+    _forward_case(synth.WORKLOADS["gptoss20b-bf16-c64-k8"])
+
+
 @pytest.mark.parametrize("K", [3, 5, 7])
 def test_forward_qwen_c16_full(K):
     """All 16 sequences of the Qwen-shaped drafter at each depth."""
