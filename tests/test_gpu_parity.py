@@ -236,7 +236,7 @@ def _random_case(seed):
     return wl, bool(r.integers(0, 2))
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(32))
 def test_forward_bf16_random_shapes(seed):
     """Seeded sweep over drafter and batch shapes (see _random_case), each
     against the oracle like the fixed cases."""
