@@ -253,7 +253,7 @@ def test_forward_bf16_row_count_boundaries(c):
     rows and c * 7 sampled rows): 16 rows (few-row kernels), 24 (the 64 x 64
     ring with 64-deep stages), 160 (a 140-row LM head whose second 128-row tile
     has an all-padding wave pair), 256 (the last row count on the 64 x 64 ring)
-    and 264 (the 128-row ring tiles)."""
+    and 264 (the 128-row ring tiles, on tile-major operands for packed models)."""
     spec = synth.ModelSpec(hidden=256, vocab=1000, n_layers=1, n_q=8, n_kv=2, head_dim=64, inter=512)
     wl = synth.Workload(f"rows-c{c}", spec, c=c, K=7, ctx_lo=10, ctx_hi=300, accept_hi=7, seed=120 + c)
     _forward_case(wl)
