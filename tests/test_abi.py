@@ -195,3 +195,58 @@ def test_noalloc_forward_rejects_batches_beyond_its_scratch(lib):
         assert lib.pe_workspace_bytes(h, 1, 7, 14) <= _lib.STATIC_SCRATCH_BYTES
     finally:
         lib.pe_model_destroy(h)
+
+
+def _up256(v):
+    return (v + 255) // 256 * 256
+
+
+def _packed_bytes_expected(H, V, n_q, n_kv, d, inter, tile_copies):
+    """Bytes of the packed copies as the header lays them out: every projection
+    in fragment order (16-row tiles of 32-deep KiB fragments), the LM head
+    tile-major (256-row groups), and, with hidden, n_q * d and inter multiples
+    of 64, every projection once more tile-major, its rows rounded up to whole
+    tiles of its ring (128 x 128 for q/k/v, 256-wide otherwise, a SiLU * up tile
+    holding 128 output columns), then to 256-row groups; each region 256-byte
+    aligned."""
+    qd, kvd = n_q * d, n_kv * d
+    mats = [(H, 2 * H), (qd + 2 * kvd, H), (H, qd), (inter, H), (inter, H), (H, inter)]
+    total = sum(_up256((nout + 15) // 16 * 16 * k * 2) for nout, k in mats)
+    total += _up256((V + 255) // 256 * 256 * H * 2)
+    if tile_copies:
+        def rows(nout, bn, cols):
+            return (nout + cols - 1) // cols * bn
+        tiles = [(rows(H, 256, 256), 2 * H), (rows(qd + 2 * kvd, 128, 128), H), (rows(H, 256, 256), qd),
+                 (rows(inter, 256, 128), H), (rows(H, 256, 256), inter)]
+        total += sum(_up256((r + 255) // 256 * 256 * k * 2) for r, k in tiles)
+    return total
+
+
+@pytest.mark.parametrize("shape,tile_copies", [
+    (dict(hidden=2880, vocab=201088, n_q=64, n_kv=8, head_dim=64, inter=7680, mask_token_id=201087), True),
+    (dict(hidden=288, vocab=1000, n_q=8, n_kv=2, head_dim=32, inter=320, mask_token_id=999), False),
+    (dict(hidden=256, vocab=1000, n_q=8, n_kv=2, head_dim=64, inter=512, mask_token_id=999), True),
+])
+def test_packed_weights_bytes_follow_the_layouts(lib, shape, tile_copies):
+    """pe_packed_weights_bytes against the layouts the header documents: the
+    GPT-OSS-shaped drafter (the tile-major projections add about 226 MB), a
+    hidden width off the 64 grid (no tile-major projections) and a small
+    drafter on it; fp32 models pack nothing."""
+    st, h = _create(lib, _desc(dtype=1, **shape))
+    assert st == 0
+    try:
+        got = lib.pe_packed_weights_bytes(h)
+        want = _packed_bytes_expected(shape["hidden"], shape["vocab"], shape["n_q"], shape["n_kv"],
+                                      shape["head_dim"], shape["inter"], tile_copies)
+        assert got == want
+        if shape["hidden"] == 2880:
+            extra = want - _packed_bytes_expected(2880, 201088, 64, 8, 64, 7680, False)
+            assert 225e6 < extra < 227e6
+    finally:
+        lib.pe_model_destroy(h)
+    st, h = _create(lib, _desc(dtype=0, **shape))
+    assert st == 0
+    try:
+        assert lib.pe_packed_weights_bytes(h) == 0
+    finally:
+        lib.pe_model_destroy(h)
