@@ -530,6 +530,8 @@ pe_status forward_impl(const pe_model* m, int32_t c, int32_t K, int32_t N, const
     at.q = qrot; at.pos = draft_pos; at.rejected = is_rejected; at.cu_draft = cu_draft;
     at.kv_lens = kv_lens; at.block_table = block_table; at.k_cache = k_cache[l];
     at.v_cache = v_cache[l]; at.partial = part; at.out = act; at.out_group = og;
+    // the ring kernels hold two workgroups per CU
+    at.fold = static_cast<int64_t>(ws.splits) * d.n_kv * c <= 2LL * cus;
     TimedScope ts(PE_KERNEL_ATTENTION, stream, timed);
     PE_HIP(pe::launch_attention(at, stream));
     return PE_OK;

@@ -434,7 +434,11 @@ __global__ __launch_bounds__(512, D == 64 || ST == 2 ? 4 : 2) void attn_ring_ker
         const int other = a.kv_lens[o];
         rank += other > mine || (other == mine && o < tid);
       }
-      if (rank == static_cast<int>(blockIdx.z)) seq_sel = tid;
+      // launch slot z takes rank z, or with `fold` the second half of the
+      // slots the remaining ranks from the shortest up
+      const int z = blockIdx.z, h = (a.c + 1) / 2;
+      const int want = a.fold && z >= h ? a.c - 1 - (z - h) : z;
+      if (rank == want) seq_sel = tid;
     }
     __syncthreads();
     i = __builtin_amdgcn_readfirstlane(seq_sel);

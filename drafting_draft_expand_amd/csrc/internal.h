@@ -220,6 +220,10 @@ struct AttnArgs {
   // out tile-major in groups of out_group rows ([N / G][n_q d / 32][G][32],
   // n_q d % 32 == 0), 0: row-major
   int out_group;
+  // every workgroup resident at once (the caller's estimate): launch slots
+  // past the middle take the remaining sequences shortest first, so that the
+  // two halves of the grid pair long with short
+  int fold;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
