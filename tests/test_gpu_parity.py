@@ -259,6 +259,16 @@ def test_forward_bf16_row_count_boundaries(c):
     _forward_case(wl)
 
 
+def test_forward_bf16_more_than_512_sequences():
+    """520 sequences at K = 2: the ring attention past its KV-length ranking
+    (at most 512 sequences; launch order beyond), 2080 draft rows on the
+    tile-major path (16.25 row groups) and 1040 sampled rows for the LM head
+    (nine 128-row tiles, the last one mostly padding)."""
+    spec = synth.ModelSpec(hidden=128, vocab=600, n_layers=1, n_q=4, n_kv=2, head_dim=64, inter=256)
+    wl = synth.Workload("many-seqs-c520", spec, c=520, K=2, ctx_lo=0, ctx_hi=60, accept_hi=2, seed=777)
+    _forward_case(wl)
+
+
 def test_forward_bf16_widths_off_the_64_grid():
     """hidden 288 at 160 rows: q/k/v and gate/up (K = 288) are off the 64-wide
     K grid of the tiled kernels, so the pass takes the unfused plan: the fc
