@@ -577,7 +577,7 @@ def main() -> int:
     if args.summarize_counters:
         return _summarize_counters(args.summarize_counters)
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+        print(json.dumps({"error": "the drafter step runs on one GPU (one GPU's share of a sharded deployment); --gpus must be 1",
                           "n_gpus_requested": args.gpus}))
         return 2
     if args.calibrate_copy:

@@ -60,7 +60,7 @@ extern "C" {
 typedef enum {
   PE_OK = 0,
   PE_EINVAL = -1,       /* bad argument (null pointer, size out of range, misaligned) */
-  PE_EUNSUPPORTED = -2, /* shape or dtype this build has no kernel for */
+  PE_EUNSUPPORTED = -2, /* shape or dtype the library has no kernel for */
   PE_EWORKSPACE = -3,   /* workspace smaller than pe_workspace_bytes() */
   PE_EHIP = -4          /* a HIP launch or runtime call failed */
 } pe_status;
