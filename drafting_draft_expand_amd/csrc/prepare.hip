@@ -12,12 +12,14 @@
 // rejected rows instead (a + K rows per sequence) and parks inert padding rows
 // after the live ones, so buffer shapes stay those of the fixed layout.
 //
-// One launch, grid (sequence, column chunk), 256 threads:
-//   * every block derives its sequence's first verified row with a block-wide
-//     reduction over the preceding query lengths (the exclusive scan of L);
-//   * column chunk 0 writes the per-row metadata of the sequence;
-//   * every block copies its column slice of all L+K-1 hidden rows of the
-//     sequence with 16-byte loads/stores, reading either the target row the
+// One launch, grid (sequence, column chunk + 1), 256 threads:
+//   * every block derives its sequence's first verified row (and, compacted,
+//     its first draft row and the live total) in one block-wide reduction over
+//     the preceding query lengths, with its own L and a loaded alongside;
+//   * the last block of each sequence writes the per-row metadata, so that
+//     no hidden-row copy waits behind the metadata's loads and stores;
+//   * every other block copies its column slice of all L+K-1 hidden rows of
+//     the sequence with 16-byte loads/stores, reading either the target row the
 //     draft row maps from or h_shared.  Each output row is written once, so
 //     placement and broadcast form a single gather with no ordering hazard.
 #include "common.h"
@@ -25,41 +27,64 @@
 namespace pe {
 namespace {
 
-// sum of v[0..n) over the block (every thread gets it); callable repeatedly
-__device__ __forceinline__ int block_prefix_sum(const int32_t* v, int n) {
-  __shared__ int part[4];
-  int s = 0;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) s += v[i];
+// Block-wide sums over j < n of v[j], and (when w is set) of w[j] for j < n
+// and j < nw; every thread gets all three.
+struct PrefixSums {
+  int v, w_lo, w_all;
+};
+__device__ __forceinline__ PrefixSums block_prefix_sums(const int32_t* v, int n, const int32_t* w, int nw) {
+  __shared__ int part[4][3];
+  int s = 0, lo = 0, all = 0;
+  for (int j = threadIdx.x; j < n; j += blockDim.x) s += v[j];
+  if (w) {
+    for (int j = threadIdx.x; j < nw; j += blockDim.x) {
+      const int x = w[j];
+      all += x;
+      lo += j < n ? x : 0;
+    }
+  }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  for (int off = 32; off >= 1; off >>= 1) {
+    s += __shfl_xor(s, off, 64);
+    lo += __shfl_xor(lo, off, 64);
+    all += __shfl_xor(all, off, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    part[threadIdx.x >> 6][0] = s;
+    part[threadIdx.x >> 6][1] = lo;
+    part[threadIdx.x >> 6][2] = all;
+  }
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
-  __syncthreads();
-  const int total = part[0] + part[1] + part[2] + part[3];
-  return total;
+  PrefixSums r;
+  r.v = part[0][0] + part[1][0] + part[2][0] + part[3][0];
+  r.w_lo = part[0][1] + part[1][1] + part[2][1] + part[3][1];
+  r.w_all = part[0][2] + part[1][2] + part[2][2] + part[3][2];
+  return r;
 }
 
 __global__ __launch_bounds__(256) void prepare_kernel(PrepareArgs a, int row_bytes, int vecs_per_row,
                                                       int vecs_per_chunk) {
   const int i = blockIdx.x;
-  const int s = block_prefix_sum(a.query_lens, i);
   const int K = a.K;
+  // this sequence's own values first: their loads overlap the reduction's
   const int L = a.query_lens[i];
   const int acc = a.num_accepted[i];
+  const PrefixSums ps = block_prefix_sums(a.query_lens, i, a.compact ? a.num_accepted : nullptr, a.c);
+  const int s = ps.v;
   // fixed layout: L + K - 1 rows per sequence (rejected rows kept, inert);
   // compacted: a + K rows (rejected rows dropped), then inert padding rows up
   // to the fixed total, sequence i padding as many rows as it dropped
   const int D_fixed = s + i * (K - 1);
   int D = D_fixed, rows = L + K - 1, live = a.N, pad0 = 0, npad = 0;
   if (a.compact) {
-    D = block_prefix_sum(a.num_accepted, i) + i * K;
+    D = ps.w_lo + i * K;
     rows = acc + K;
-    live = block_prefix_sum(a.num_accepted, a.c) + a.c * K;
+    live = ps.w_all + a.c * K;
     pad0 = live + (D_fixed - D);
     npad = L - 1 - acc;
   }
 
-  if (blockIdx.y == 0) {
+  if (blockIdx.y == gridDim.y - 1) {
     const int bonus = a.bonus_ids[i];
     const int base = a.target_pos[s + acc];
     const int bs = a.block_size;
@@ -104,6 +129,7 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepareArgs a, int row_byt
       a.kv_lens[i] = base + K;
       if (i == a.c - 1) a.cu_draft[a.c] = live;
     }
+    return;
   }
 
   // hidden placement: gather of 16-byte vectors for this block's column slice
@@ -219,7 +245,8 @@ hipError_t launch_prepare(const PrepareArgs& a, hipStream_t stream) {
   if (chunks > max_chunks) chunks = max_chunks;
   const int per_chunk = (vecs + chunks - 1) / chunks;
   chunks = (vecs + per_chunk - 1) / per_chunk;
-  dim3 grid(a.c, chunks);
+  // the column chunks, then one metadata block per sequence
+  dim3 grid(a.c, chunks + 1);
   hipLaunchKernelGGL(prepare_kernel, grid, dim3(256), 0, stream, a, row_bytes, vecs, per_chunk);
   return hipGetLastError();
 }
