@@ -335,6 +335,18 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
         }
       }
     }
+    // q/k/v epilogue: the rotary cos/sin of the tile this wave finishes, read
+    // before the weights stream rather than after it (clamped rows and tiles
+    // read valid entries that the epilogue does not use)
+    float2 rot[4];
+    if constexpr (EPI == Epi::QkvRope) {
+      const int d = a.rope.d;
+      const int n = tile_row<EPI>(a, min(g * NT + min(wave, NT - 1), T - 1), lane & 15);
+      const int jj = (n % d) % (d / 2);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        rot[q] = a.rope.table[static_cast<int64_t>(min(4 * j + q, a.M - 1)) * (d / 2) + jj];
+    }
     f32x4 acc[NT][NB];
 #pragma unroll
     for (int n = 0; n < NT; ++n)
@@ -448,7 +460,6 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
         const int d = ro.d;
         const int head = n / d;
         const int e = n - head * d;                  // element within the head
-        const int jj = e % (d / 2);                  // rotary pair index
         const bool rotate = head < ro.n_q + ro.n_kv;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -457,10 +468,7 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
           const float partner = __shfl_xor(v, 8, 64);
           if (!r_live[q]) continue;
           float out = v;
-          if (rotate) {
-            const float2 t = ro.table[static_cast<int64_t>(m) * (d / 2) + jj];
-            out = c < 8 ? v * t.x - partner * t.y : v * t.x + partner * t.y;
-          }
+          if (rotate) out = c < 8 ? v * rot[q].x - partner * rot[q].y : v * rot[q].x + partner * rot[q].y;
           if (head < ro.n_q) {
             static_cast<bf16_t*>(ro.q_out)[(static_cast<int64_t>(m) * ro.n_q + head) * d + e] = f32_to_bf16(out);
           } else {
