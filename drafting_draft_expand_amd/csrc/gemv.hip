@@ -277,6 +277,13 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
     __syncthreads();
   }
   const float inv = (MODE == AMode::Norm && xvalid) ? inv_s[lane & 15] : 0.f;
+  // gathered operand [emb(id) ; h]: the token id is requested once, here, and
+  // each step's piece is addressed by a select between the two row halves (a
+  // per-step id load behind a branch costs a round trip per step, each
+  // waiting for every load issued before it)
+  const int half_k = MODE == AMode::Gather ? K / 2 : 0;
+  int idm = 0;
+  if constexpr (MODE == AMode::Gather) idm = a.ids[mclamp];
   const int T = (a.Nout + 15) / 16;
   const int G = (T + NT - 1) / NT;
   // q/k/v epilogue: the rejected flag and cache slot of this lane's
@@ -356,14 +363,34 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
       // Issue order: the A fragments (cache hits) first, then the B fragments
       // step by step, all before the first product; the barrier keeps the
       // scheduler from sinking loads below products, so the products of step
-      // u wait only for the loads of steps <= u.
+      // u wait only for the loads of steps <= u.  A gathered operand goes
+      // last instead: its addresses wait for the token ids, and the weight
+      // stream should not wait with them.
       u32x4 av[U], bv[U][NT][NB];
+      auto load_a = [&]() __attribute__((always_inline)) {
+        if constexpr (MODE == AMode::Gather) {
+          // the id is first needed here, after the weight loads: the empty asm
+          // keeps the row address from being formed (and the id waited for)
+          // ahead of them
+          int id = idm;
+          asm volatile("" : "+v"(id));
+          const bf16_t* erow = static_cast<const bf16_t*>(a.embed) + static_cast<int64_t>(id) * half_k;
+          const bf16_t* hrow = static_cast<const bf16_t*>(a.x2) + static_cast<int64_t>(mclamp) * half_k - half_k;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int ss = min(s + u, slast);
-        const u32x4 x = load_a16<bf16_t, MODE>(a, mclamp, 4 * ss + j, inv);
-        av[u] = (s + u < ks1 && xvalid) ? x : zero;
-      }
+          for (int u = 0; u < U; ++u) {
+            const int k = (4 * min(s + u, slast) + j) * 8;
+            av[u] = load16(k < half_k ? erow + k : hrow + k);
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int ss = min(s + u, slast);
+            const u32x4 x = load_a16<bf16_t, MODE>(a, mclamp, 4 * ss + j, inv);
+            av[u] = (s + u < ks1 && xvalid) ? x : zero;
+          }
+        }
+      };
+      if constexpr (MODE != AMode::Gather) load_a();
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int ss = min(s + u, slast);
@@ -378,7 +405,14 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
               bv[u][n][b] = load16_stream(wp[n][b] + static_cast<int64_t>(ss) * WSTEP);
           }
       }
+      if constexpr (MODE == AMode::Gather) load_a();
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (MODE == AMode::Gather) {
+        // steps past the range and padding rows multiply zeros (applied only
+        // now, so that no load waits for another)
+#pragma unroll
+        for (int u = 0; u < U; ++u) av[u] = (s + u < ks1 && xvalid) ? av[u] : zero;
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
