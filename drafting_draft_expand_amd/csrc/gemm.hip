@@ -516,7 +516,17 @@ __global__ __launch_bounds__(256, ST * (BM + BN) * BKS * 2 > 80 * 1024 ? 1 : 2) 
   const int mt = L % num_m, rest = L / num_m;
   const int z = rest % splits, nt = rest / splits;
   const int m0 = mt * BM;
-  if (a.m_live && m0 >= *a.m_live) return;
+  // A tile of padding rows only (compacted layout) stops once its first copies
+  // have landed.  The live count is read (scalar load) just before the first
+  // copies are requested and tested after them, so that live tiles do not
+  // wait for it first; read after the copies (which clobber memory as far as
+  // the compiler knows) it would become a vector load whose wait drains them.
+  int live_rows = 0x7fffffff;
+  auto read_live = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (a.m_live) live_rows = *a.m_live;
+  };
+  auto padding_tile = [&]() __attribute__((always_inline)) { return m0 >= live_rows; };
   const int nk_all = a.K / BK;
   const int per_split = (nk_all + splits - 1) / splits;
   const int kbase = min(nk_all, z * per_split);
@@ -626,12 +636,17 @@ __global__ __launch_bounds__(256, ST * (BM + BN) * BKS * 2 > 80 * 1024 ? 1 : 2) 
     // every barrier, but reads no fragments and runs no MFMAs: its SIMD goes
     // to the other workgroup on the CU.  Its accumulators stay zero, and the
     // epilogue writes no row past M.
-    auto run = [&](auto live_c) __attribute__((always_inline)) {
+    auto run = [&](auto live_c) __attribute__((always_inline)) -> bool {
       constexpr bool LIVE = decltype(live_c)::value;
       // prologue: steps 0 .. ST-1 requested, stages 0 and 1 landed
       // everywhere, step 0's fragments in registers and every wave done
       // reading slot 0
+      read_live();
       static_for<ST>([&](auto s_c) { request(decltype(s_c)::value, s_c); });
+      if (padding_tile()) {
+        __builtin_amdgcn_s_waitcnt(0);
+        return false;
+      }
       sync();
       if constexpr (LIVE) frags(C0{}, C0{});
       sync();
@@ -657,11 +672,17 @@ __global__ __launch_bounds__(256, ST * (BM + BN) * BKS * 2 > 80 * 1024 ? 1 : 2) 
       static_for<U - 1>([&](auto j_c) {
         if (t + decltype(j_c)::value < nk) step(t + decltype(j_c)::value, j_c);
       });
+      return true;
     };
-    if (m0 + wm * WM < a.M) run(std::true_type{});
-    else run(std::false_type{});
+    const bool go = m0 + wm * WM < a.M ? run(std::true_type{}) : run(std::false_type{});
+    if (!go) return;
   } else {
+    read_live();
     static_for<ST - 1>([&](auto s_c) { request(decltype(s_c)::value, s_c); });
+    if (padding_tile()) {
+      __builtin_amdgcn_s_waitcnt(0);
+      return;
+    }
     auto step = [&](int t, auto s_c) __attribute__((always_inline)) {
       constexpr int S = decltype(s_c)::value;
       sync();

@@ -261,7 +261,8 @@ __global__ __launch_bounds__(64 * SK) void mfma_skinny_kernel(GemvArgs a) {
   const int ks0 = min(kz1, kz0 + wave * per);
   const int ks1 = min(kz1, ks0 + per);
   const int slast = max(ks0, ks1 - 1);             // clamp target (never read when ks0 == ks1)
-  if (a.m_live && *a.m_live <= 0) return;          // only padding rows
+  // (the live-row count a.m_live is not read: the one 16-row fragment always
+  // holds a live row, and padding rows are computed like the others)
   const int mrow = lane & 15;
   const bool xvalid = mrow < a.M;
   const int mclamp = min(mrow, a.M - 1);

@@ -54,13 +54,19 @@ __global__ __launch_bounds__(1024) void rmsnorm_kernel(int H, const int32_t* __r
     rope_cos_sin(rt.pos[i], rt.freq.inv[threadIdx.x], c, s);
     rt.out[static_cast<int64_t>(i) * rt.half + threadIdx.x] = make_float2(c, s);
   }
-  if (live && i >= *live) return;  // padding row of the compacted layout
   const int r = row_idx ? row_idx[i] : i;
   f32x4* xr = reinterpret_cast<f32x4*>(x + static_cast<int64_t>(r) * H);
   const int nv = H / 4;
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   f32x4 keep[2];
   float ss = 0.f;
+  int nlive;
+  // the gains are requested with the row, so that their latency overlaps the
+  // row's and the reduction
+  f32x4 gv[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    gv[u] = load4_f32(gain + 4 * min(static_cast<int>(threadIdx.x + blockDim.x * u), nv - 1));
   {
     f32x4 xv[2], pv[2][NS > 0 ? NS : 1];
 #pragma unroll
@@ -71,6 +77,12 @@ __global__ __launch_bounds__(1024) void rmsnorm_kernel(int H, const int32_t* __r
       for (int z = 0; z < NS; ++z)
         pv[u][z] = reinterpret_cast<const f32x4*>(part + z * part_stride + static_cast<int64_t>(r) * H)[v];
     }
+    // padding row of the compacted layout (nothing stored): the live count is
+    // requested only now, after the row's loads (the compiler barrier keeps it
+    // there), and tested once the row has arrived, so the row does not wait
+    // for it (a scalar load waited for early would hold back every later one)
+    asm volatile("" : : : "memory");
+    nlive = live ? *live : 0x7fffffff;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       f32x4 q = xv[u];
@@ -78,16 +90,18 @@ __global__ __launch_bounds__(1024) void rmsnorm_kernel(int H, const int32_t* __r
       for (int z = 0; z < NS; ++z) q += pv[u][z];
       const bool mine = static_cast<int>(threadIdx.x + blockDim.x * u) < nv;
       q = mine ? q : zero;
-      if (NS > 0 && mine) xr[threadIdx.x + blockDim.x * u] = q;
       keep[u] = q;
       ss += q[0] * q[0] + q[1] * q[1] + q[2] * q[2] + q[3] * q[3];
     }
   }
-  // the gains are loaded before the reduction so that their latency overlaps it
-  f32x4 gv[2];
+  // (the sum above is formed on every path, so the row loads stay ahead of the test)
+  asm volatile("" : : "v"(ss));
+  if (i >= nlive) return;
+  if (NS > 0) {
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
-    gv[u] = load4_f32(gain + 4 * min(static_cast<int>(threadIdx.x + blockDim.x * u), nv - 1));
+    for (int u = 0; u < 2; ++u)
+      if (static_cast<int>(threadIdx.x + blockDim.x * u) < nv) xr[threadIdx.x + blockDim.x * u] = keep[u];
+  }
   ss = wave_sum(ss);
   const int nw = blockDim.x >> 6;
   if ((threadIdx.x & 63) == 0) wave_ss[threadIdx.x >> 6] = ss;
