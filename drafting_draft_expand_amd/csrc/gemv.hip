@@ -108,11 +108,22 @@ __global__ __launch_bounds__(256) void gemv_lds_kernel(GemvArgs a) {
       }
       __syncthreads();
     }
+    // eight pieces per thread requested before any is stored (one at a time,
+    // each LDS store would wait for its load: a round trip per piece)
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    for (int v = threadIdx.x; v < MT * KV; v += blockDim.x) {
-      const int m = v / KV;
-      xs[v] = m < mcount ? load_a16<TW, MODE>(a, m0 + m, v - m * KV, MODE == AMode::Norm ? inv_s[m] : 0.f)
-                         : zero;
+    constexpr int SU = 8;
+    for (int v0 = threadIdx.x; v0 < MT * KV; v0 += blockDim.x * SU) {
+      u32x4 piece[SU];
+#pragma unroll
+      for (int u = 0; u < SU; ++u) {
+        const int v = min(v0 + u * static_cast<int>(blockDim.x), MT * KV - 1);
+        const int m = v / KV;
+        piece[u] = m < mcount ? load_a16<TW, MODE>(a, m0 + m, v - m * KV, MODE == AMode::Norm ? inv_s[m] : 0.f)
+                              : zero;
+      }
+#pragma unroll
+      for (int u = 0; u < SU; ++u)
+        if (v0 + u * static_cast<int>(blockDim.x) < MT * KV) xs[v0 + u * blockDim.x] = piece[u];
     }
     __syncthreads();
   }
