@@ -96,7 +96,11 @@ __global__ __launch_bounds__(1024) void rmsnorm_kernel(int H, const int32_t* __r
   }
   // (the sum above is formed on every path, so the row loads stay ahead of the test)
   asm volatile("" : : "v"(ss));
-  if (i >= nlive) return;
+  if (i >= nlive) {
+    // (the gains, still in flight, are waited for before the wave ends)
+    asm volatile("" : : "v"(gv[0]), "v"(gv[1]));
+    return;
+  }
   if (NS > 0) {
 #pragma unroll
     for (int u = 0; u < 2; ++u)
