@@ -29,7 +29,9 @@ def _ring_bodies(tmp_path, source, kernel):
     subprocess.run(cmd, check=True, capture_output=True)
     text = out.read_text()
     bodies = {}
-    for m in re.finditer(r"^(_Z\S*" + kernel + r"\S*):.*?\n(.*?)s_endpgm", text, re.S | re.M):
+    # the whole function, up to its end label: the compiler may place blocks
+    # (copies included) after an s_endpgm
+    for m in re.finditer(r"^(_Z\S*" + kernel + r"\S*):.*?\n(.*?)^\.Lfunc_end", text, re.S | re.M):
         bodies[m.group(1)] = [ln.strip() for ln in m.group(2).split("\n")
                               if ln.strip() and not ln.strip().startswith(";")]
     return bodies
