@@ -864,7 +864,11 @@ hipError_t launch_cfg(GemvArgs& a, int num_cus, hipStream_t s) {
   if ((EPI == Epi::Store || EPI == Epi::AddTo) && a.part && !a.ss_out &&
       tiles_of(t, a.M, a.Nout, EPI) < 2 * num_cus)
     t = kMedium;
-  if (t.bn == 256) return launch_t<128, 256, 32, 2, 2, EPI, MODE>(a, num_cus, s);
+  if (t.bn == 256) {
+    // (never chosen for q/k/v, whose epilogue does not fit this tile's registers)
+    if constexpr (EPI == Epi::QkvRope) return hipErrorInvalidValue;
+    else return launch_t<128, 256, 32, 2, 2, EPI, MODE>(a, num_cus, s);
+  }
   if (t.bn == 128) return launch_t<128, 128, 64, 2, 2, EPI, MODE>(a, num_cus, s);
   return launch_t<128, 64, 64, 2, 2, EPI, MODE>(a, num_cus, s);
 }
