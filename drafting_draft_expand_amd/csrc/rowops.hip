@@ -243,6 +243,20 @@ hipError_t launch_build_fc_input(DType dt, int N, int H, const int32_t* ids, con
 }
 
 namespace {
+// Compute units of the current device (queried once per device).
+constexpr int kMaxWavesPerCu = 32;
+int device_cus() {
+  static int cached[16] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 256;
+  if (cached[dev] == 0) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    cached[dev] = c;
+  }
+  return cached[dev];
+}
+
 template <typename T, int NS>
 void launch_rmsnorm_t(int rows, int H, const int32_t* row_idx, float* x, const void* gain, float eps, void* out,
                       hipStream_t s, const int32_t* live, const float* part, int64_t stride, bool accumulate,
@@ -250,7 +264,18 @@ void launch_rmsnorm_t(int rows, int H, const int32_t* row_idx, float* x, const v
   const int nv = H / 4;
   int threads = ((nv + 1) / 2 + 63) / 64 * 64;  // at most two pieces per thread
   if (threads < 64) threads = 64;
-  if (nv <= 1024) threads = (nv + 63) / 64 * 64;  // one piece per thread while that fits
+  if (nv <= 1024) {
+    // one piece per thread while that fits, unless two per thread (half the
+    // waves per row) keep every row resident in fewer rounds: 896 rows of
+    // 2880 take two rounds at 12 waves per row and one at 6
+    const int one = (nv + 63) / 64 * 64;
+    auto rounds = [&](int th) {
+      const int per_cu = kMaxWavesPerCu / (th / 64);
+      const int64_t slots = static_cast<int64_t>(device_cus()) * (per_cu > 0 ? per_cu : 1);
+      return (rows + slots - 1) / slots;
+    };
+    threads = rounds(threads) < rounds(one) ? threads : one;
+  }
   if (threads < rt.half) threads = (rt.half + 63) / 64 * 64;
   hipLaunchKernelGGL((rmsnorm_kernel<T, NS>), dim3(rows), dim3(threads), 0, s, H, row_idx, x,
                      static_cast<const T*>(gain), eps, static_cast<T*>(out), live, part, stride, int(accumulate),
