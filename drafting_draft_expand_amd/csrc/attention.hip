@@ -661,33 +661,30 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int h0 = (blockIdx.y * 4 + (threadIdx.x >> 6)) * HPW;  // this wave's first head
   const int S = a.splits;                                      // 1 <= S <= MAXS
   const bool rejected = a.rejected[row];
-  // HPW heads per wave, unrolled so that their loads are in flight together
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) {
-    const int h = h0 + hh;
-    if (h >= a.n_q) break;
-    // element h D + e of the row: row-major, or tile-major in groups of
-    // out_group rows (32-element pieces of one row contiguous)
-    const int G = a.out_group;
-    auto out_at = [&](int e) -> int64_t {
-      const int64_t k = static_cast<int64_t>(h) * D + e;
-      if (G == 0) return static_cast<int64_t>(row) * a.n_q * D + k;
-      return (static_cast<int64_t>(row / G) * (a.n_q * D / 32) + k / 32) * G * 32 + (row % G) * 32 + (k & 31);
-    };
-    T* out = static_cast<T*>(a.out);
-    // (a rejected row's partials were never written: they are read with the
-    // rest, so no load waits for the flag, and discarded)
+  const int sl = min(lane, S - 1);
+  // (a rejected row's partials were never written: they are read with the
+  // rest, so no load waits for the flag, and discarded)
+  auto load_head = [&](int h, float& m_l, float& l_l, float (&v)[DV][MAXS]) __attribute__((always_inline)) {
     const float* p = a.partial + (static_cast<int64_t>(row) * a.n_q + h) * S * (D + 2);
-    const int sl = min(lane, S - 1);
-    const float m_l = p[sl * (D + 2) + D];
-    const float l_l = p[sl * (D + 2) + D + 1];
-    float v[DV][MAXS];
+    m_l = p[sl * (D + 2) + D];
+    l_l = p[sl * (D + 2) + D + 1];
 #pragma unroll
     for (int z = 0; z < MAXS; ++z) {
       const int zc = min(z, S - 1);
 #pragma unroll
       for (int e = 0; e < DV; ++e) v[e][z] = p[zc * (D + 2) + min(lane + 64 * e, D - 1)];
     }
+  };
+  // element h D + e of the row: row-major, or tile-major in groups of
+  // out_group rows (32-element pieces of one row contiguous)
+  const int G = a.out_group;
+  T* out = static_cast<T*>(a.out);
+  auto merge_store = [&](int h, float m_l, float l_l, const float (&v)[DV][MAXS]) __attribute__((always_inline)) {
+    auto out_at = [&](int e) -> int64_t {
+      const int64_t k = static_cast<int64_t>(h) * D + e;
+      if (G == 0) return static_cast<int64_t>(row) * a.n_q * D + k;
+      return (static_cast<int64_t>(row / G) * (a.n_q * D / 32) + k / 32) * G * 32 + (row % G) * 32 + (k & 31);
+    };
     const float ms = lane < S ? m_l : -INFINITY;
     const float M = wave_max(ms);
     const float w = ms == -INFINITY ? 0.f : expf(ms - M);
@@ -705,6 +702,31 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < DV; ++e)
       if (lane + 64 * e < D) out[out_at(lane + 64 * e)] = Elem<T>::from_f32(rejected ? 0.f : num[e] * inv);
+  };
+  if constexpr (MAXS <= 2) {
+    // few splits: every head's loads go out before any store (head by head,
+    // a head's loads would queue behind the previous head's stores, which
+    // may alias them as far as the compiler knows); heads past n_q re-read
+    // the last head and are not stored.  (With more splits the wider loads
+    // of all heads at once measured slower.)
+    float m_l[HPW], l_l[HPW], v[HPW][DV][MAXS];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) load_head(min(h0 + hh, a.n_q - 1), m_l[hh], l_l[hh], v[hh]);
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      if (h0 + hh >= a.n_q) break;
+      merge_store(h0 + hh, m_l[hh], l_l[hh], v[hh]);
+    }
+  } else {
+    // HPW heads per wave, unrolled so that their loads are in flight together
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      const int h = h0 + hh;
+      if (h >= a.n_q) break;
+      float m_l, l_l, v[DV][MAXS];
+      load_head(h, m_l, l_l, v);
+      merge_store(h, m_l, l_l, v);
+    }
   }
 }
 
